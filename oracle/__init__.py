@@ -1,0 +1,200 @@
+"""CPU oracle for MoE expert-parallel dispatch/combine (ctypes over epx_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers. The product library never imports,
+links or executes anything here, and nothing here imports the product.
+
+Each wrapper takes and returns numpy arrays; the arithmetic lives in
+``epx_oracle.c`` (plain scalar loops written from the definitions in the
+digest "Balancing and Beyond: Communication-Centric Optimizations in Expert
+Parallelism", sections 1-3, and in the DeepEP issue "[GH-ISSUE #250]
+Profiling when rank unbalance").
+
+Parity status of each function (what pins it, in tests/test_oracle_*.py):
+  layout         -- brute-force enumeration of the order definitions on small
+                    inputs; invariants; the copy-count closed forms of digest
+                    section 3.2; the worked example of the DeepEP issue.
+  dispatch_bf16  -- row equality with the token's row (definition) on small inputs.
+  dispatch_fp8   -- converter exhaustive vs torch's float8_e4m3fn cast; block
+                    properties (amax code is 448, error bound of a 3-bit mantissa).
+  combine        -- float64 sum within the float32 error bound; exact special cases.
+  relay row order, zero-block rule, fma order: parity unpinned by the pages
+                    (fixed by the readings recorded in the design notes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "epx_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-std=c11"]
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def build(out: str = _LIB, extra_flags=()) -> str:
+    """Compile the oracle with gcc (plain C, libm only)."""
+    cmd = ["gcc", *_CFLAGS, *extra_flags, "-o", out, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(path: str = _LIB) -> ctypes.CDLL:
+    """Load the oracle library, compiling it first if it is missing or stale."""
+    global _lib
+    if path == _LIB and _lib is not None:
+        return _lib
+    if (not os.path.exists(path)) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+        if path != _LIB:
+            raise FileNotFoundError(path)
+        build(path)
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    lib.oracle_layout.argtypes = [i32] * 7 + [P] * 16
+    lib.oracle_layout.restype = ctypes.c_int
+    lib.oracle_dispatch_bf16.argtypes = [i32] * 5 + [P] * 4
+    lib.oracle_dispatch_bf16.restype = ctypes.c_int
+    lib.oracle_dispatch_fp8.argtypes = [i32] * 5 + [P] * 5
+    lib.oracle_dispatch_fp8.restype = ctypes.c_int
+    lib.oracle_combine.argtypes = [i32] * 3 + [P] * 4
+    lib.oracle_combine.restype = ctypes.c_int
+    for name in ("oracle_f32_to_e4m3_array", "oracle_f32_to_bf16_array", "oracle_e4m3_to_f32_array"):
+        getattr(lib, name).argtypes = [P, P, ctypes.c_int64]
+        getattr(lib, name).restype = None
+    if path == _LIB:
+        _lib = lib
+    return lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: oracle status {code}")
+        self.code = code
+
+
+def layout(topk_idx: np.ndarray, num_experts: int, num_ranks: int, num_hosts: int,
+           my_rank: int = 0, relay: bool = False, lib: Optional[ctypes.CDLL] = None) -> dict:
+    """All layout arrays for one source rank (see oracle_layout in epx_oracle.c)."""
+    lib = lib or load()
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, k = idx.shape
+    E, R, H = num_experts, num_ranks, num_hosts
+    cap = T * min(k, H)
+    out = {
+        "expert_count": np.zeros(E, np.int32), "expert_offset": np.zeros(E + 1, np.int32),
+        "rank_rows": np.zeros(R, np.int32), "rank_tokens": np.zeros(R, np.int32),
+        "rank_offset": np.zeros(R + 1, np.int32), "host_tokens": np.zeros(H, np.int32),
+        "host_offset": np.zeros(H + 1, np.int32), "slot": np.zeros(T * k, np.int32),
+        "row_token": np.zeros(T * k, np.int32), "relay_slot": np.zeros(T * H, np.int32),
+        "relay_token": np.zeros(cap, np.int32), "fanout_expert": np.zeros(cap * k, np.int32),
+        "fanout_rank_mask": np.zeros(cap, np.uint32), "relay_dst_rank": np.zeros(H, np.int32),
+        "totals": np.zeros(4, np.int32),
+    }
+    rc = lib.oracle_layout(T, k, E, R, H, my_rank, int(relay), _p(idx),
+                           *[_p(out[n]) for n in (
+                               "expert_count", "expert_offset", "rank_rows", "rank_tokens",
+                               "rank_offset", "host_tokens", "host_offset", "slot", "row_token",
+                               "relay_slot", "relay_token", "fanout_expert", "fanout_rank_mask",
+                               "relay_dst_rank", "totals")])
+    out["status"] = rc
+    if rc != 0:
+        raise OracleError(rc, "oracle_layout")
+    if not relay:
+        for n in ("relay_slot", "relay_token", "fanout_expert", "fanout_rank_mask"):
+            out.pop(n)
+    return out
+
+
+def dispatch_bf16(x_bits: np.ndarray, lay: dict, topk: int, num_hosts: int, relay: bool,
+                  rows: Optional[int] = None, lib=None) -> np.ndarray:
+    """recv rows (uint16 bf16 bits) for per-expert or relay mode."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, hidden = x.shape
+    if rows is None:
+        rows = int(lay["totals"][1] if relay else lay["totals"][0])
+    recv = np.zeros((max(rows, 0), hidden), np.uint16)
+    slot = lay["slot"]
+    rslot = lay.get("relay_slot", np.zeros(1, np.int32)) if relay else np.zeros(1, np.int32)
+    rc = lib.oracle_dispatch_bf16(T, topk, num_hosts, int(relay), hidden, _p(slot), _p(rslot),
+                                  _p(x), _p(recv))
+    if rc != 0:
+        raise OracleError(rc, "oracle_dispatch_bf16")
+    return recv
+
+
+def dispatch_fp8(x_bits: np.ndarray, lay: dict, topk: int, num_hosts: int, relay: bool,
+                 rows: Optional[int] = None, lib=None):
+    """(codes uint8 [rows, h], scales float32 [rows, h/128])."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, hidden = x.shape
+    if rows is None:
+        rows = int(lay["totals"][1] if relay else lay["totals"][0])
+    q = np.zeros((rows, hidden), np.uint8)
+    sc = np.zeros((rows, hidden // 128), np.float32)
+    slot = lay["slot"]
+    rslot = lay.get("relay_slot", np.zeros(1, np.int32)) if relay else np.zeros(1, np.int32)
+    rc = lib.oracle_dispatch_fp8(T, topk, num_hosts, int(relay), hidden, _p(slot), _p(rslot),
+                                 _p(x), _p(q), _p(sc))
+    if rc != 0:
+        raise OracleError(rc, "oracle_dispatch_fp8")
+    return q, sc
+
+
+def combine(y_bits: np.ndarray, lay: dict, topk_weights: np.ndarray, lib=None) -> np.ndarray:
+    """out [T, h] uint16 bf16 bits."""
+    lib = lib or load()
+    y = np.ascontiguousarray(y_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(topk_weights, dtype=np.float32)
+    T, k = w.shape
+    hidden = y.shape[1]
+    out = np.zeros((T, hidden), np.uint16)
+    rc = lib.oracle_combine(T, k, hidden, _p(lay["slot"]), _p(w), _p(y), _p(out))
+    if rc != 0:
+        raise OracleError(rc, "oracle_combine")
+    return out
+
+
+def f32_to_e4m3(a: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load()
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, np.uint8)
+    lib.oracle_f32_to_e4m3_array(_p(a), _p(out), a.size)
+    return out
+
+
+def e4m3_to_f32(q: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    out = np.empty(q.shape, np.float32)
+    lib.oracle_e4m3_to_f32_array(_p(q), _p(out), q.size)
+    return out
+
+
+def f32_to_bf16(a: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load()
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.empty(a.shape, np.uint16)
+    lib.oracle_f32_to_bf16_array(_p(a), _p(out), a.size)
+    return out
+
+
+def expert_of_rows(lay: dict) -> np.ndarray:
+    """Expert id of each per-expert row, read off the offsets (row r belongs to
+    the expert e with expert_offset[e] <= r < expert_offset[e+1])."""
+    off = lay["expert_offset"]
+    rows = int(off[-1])
+    return (np.searchsorted(off, np.arange(rows), side="right") - 1).astype(np.int32)

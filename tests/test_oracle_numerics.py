@@ -1,0 +1,255 @@
+"""Pins of the oracle's number formats, fp8 dispatch and combine.
+
+* fp32 -> E4M3FN (saturating, nearest-even) against torch's float8_e4m3fn
+  cast after a clamp to +-448 (a library routine), exhaustively over every
+  non-negative finite float32 pattern; negatives by sign symmetry plus a
+  random sample against torch.
+* E4M3FN -> fp32 for all 256 codes against torch.
+* fp32 -> bf16 (nearest-even) against torch's bfloat16 cast over every
+  16-bit low half for a spread of high halves (the rounding decision depends
+  on the low half and the last kept bit only), and every high half for a set
+  of low halves.
+* fp8 blocks: the block maximum encodes to +-448, the scale times 448 gives
+  back the maximum, every code is within the error of a 3-bit mantissa, an
+  all-zero block keeps signed zeros, and the row size fits the byte counters
+  printed by the HybridEP issue.
+* combine: within the float32 accumulation bound of a float64 sum; exact in
+  the special cases k = 1 / one-hot weights; identity experts return x.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_epx_get_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def torch_e4m3(a: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).clamp(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def torch_bf16(a: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.slow
+def test_e4m3_exhaustive_nonnegative_vs_torch():
+    chunk = 1 << 25
+    end = 0x7F800000          # +inf; everything below is a finite non-negative float
+    for start in range(0, end, chunk):
+        bits = np.arange(start, min(start + chunk, end), dtype=np.uint32)
+        v = bits.view(np.float32)
+        got = oracle.f32_to_e4m3(v)
+        want = torch_e4m3(v)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (hex(int(bits[bad[0]])), got[bad[0]], want[bad[0]])
+
+
+def test_e4m3_sign_symmetry_and_negative_sample():
+    rng = np.random.Generator(np.random.PCG64(11))
+    bits = rng.integers(0, 0x7F800000, size=1 << 22, dtype=np.uint32)
+    v = bits.view(np.float32)
+    pos = oracle.f32_to_e4m3(v)
+    neg = oracle.f32_to_e4m3(-v)
+    assert np.array_equal(neg, pos | 0x80)
+    assert np.array_equal(neg, torch_e4m3(-v))
+
+
+def test_e4m3_critical_points():
+    """Rounding boundaries of the format, each against torch."""
+    pts = [0.0, 2.0 ** -10, 2.0 ** -9, 1.5 * 2 ** -9, 2.5 * 2 ** -9, 7.5 * 2 ** -9, 2.0 ** -6,
+           1.0, 1.0625, 1.1875, 240.0, 416.0, 447.99, 448.0, 463.99, 464.0, 470.0, 1e30, 3.4e38]
+    v = np.array(pts + [-p for p in pts], np.float32)
+    assert np.array_equal(oracle.f32_to_e4m3(v), torch_e4m3(v))
+    assert oracle.f32_to_e4m3(np.array([448.0], np.float32))[0] == 0x7E
+    assert oracle.f32_to_e4m3(np.array([2.0 ** -10], np.float32))[0] == 0x00   # tie to even (0)
+
+
+def test_e4m3_decode_all_codes_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.e4m3_to_f32(codes)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+    # the largest finite value is 448 (0x7E), the smallest subnormal 2^-9
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_bf16_rounding_vs_torch():
+    rng = np.random.Generator(np.random.PCG64(12))
+    lows = np.arange(1 << 16, dtype=np.uint32)
+    highs = np.concatenate([np.arange(0, 8), np.arange(0x007C, 0x0084), np.arange(0x3F7C, 0x3F84),
+                            np.arange(0x7F78, 0x7F80), rng.integers(0, 0x7F80, 96)]).astype(np.uint32)
+    for sign in (0, 0x8000):
+        bits = (((highs[:, None] | sign) << 16) | lows[None, :]).ravel()
+        v = bits.view(np.float32)
+        fin = np.isfinite(v)
+        assert np.array_equal(oracle.f32_to_bf16(v[fin]), torch_bf16(v[fin]))
+    all_highs = np.arange(1 << 16, dtype=np.uint32)
+    some_lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x4000, 0xC000], np.uint32)
+    bits = ((all_highs[:, None] << 16) | some_lows[None, :]).ravel()
+    v = bits.view(np.float32)
+    fin = np.isfinite(v)
+    assert np.array_equal(oracle.f32_to_bf16(v[fin]), torch_bf16(v[fin]))
+
+
+# ---------------------------------------------------------------- fp8 dispatch
+def _fp8_case(T=48, hidden=512, seed=5, outliers=True):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((T, hidden), dtype=np.float32)
+    if outliers:
+        x[:, rng.choice(hidden, 5, replace=False)] *= 50
+    x[3, 128:256] = 0.0                              # an all-zero block
+    x[4, 0:128] = -0.0                               # an all-negative-zero block
+    x[5, 256:384] *= 1e-30                           # a tiny block (float32 subnormal scale)
+    xb = W.f32_to_bf16_bits(x)
+    idx = W.draw_routing(rng, T, 16, 2, "uniform")
+    return xb, idx
+
+
+@pytest.mark.parametrize("relay", [False, True])
+def test_fp8_block_properties(relay):
+    xb, idx = _fp8_case()
+    T, hidden = xb.shape
+    lay = oracle.layout(idx, 16, 4, 2, 1, relay=relay)
+    q, sc = oracle.dispatch_fp8(xb, lay, 2, 2, relay)
+    xf = W.bf16_bits_to_f32(xb)
+    nb = hidden // 128
+    dest = lay["relay_slot"].reshape(T, 2) if relay else lay["slot"].reshape(T, 2)
+    for t in range(T):
+        rows = [r for r in dest[t] if r >= 0]
+        assert rows
+        for r in rows[1:]:                              # every copy of a token is identical
+            assert np.array_equal(q[r], q[rows[0]]) and np.array_equal(sc[r], sc[rows[0]])
+        r = rows[0]
+        for b in range(nb):
+            blk = xf[t, b * 128:(b + 1) * 128]
+            a = np.abs(blk).max()
+            s = sc[r, b]
+            codes = q[r, b * 128:(b + 1) * 128]
+            if a == 0:
+                assert s == 0
+                assert np.array_equal(codes, np.where(np.signbit(blk), 0x80, 0x00).astype(np.uint8))
+                continue
+            # scale * 448 recovers the block maximum within one float32 rounding
+            assert abs(np.float64(s) * 448 - a) <= a * 2.0 ** -23
+            # the maximum's code is +-448
+            am = np.argmax(np.abs(blk))
+            assert codes[am] & 0x7F == 0x7E
+            # every value within a 3-bit-mantissa rounding (plus the subnormal
+            # grid near zero and one float32 rounding of the quotient)
+            deq = oracle.e4m3_to_f32(codes).astype(np.float64) * s
+            err = np.abs(deq - blk)
+            bound = np.maximum(np.abs(blk) * 2.0 ** -4, s * 2.0 ** -10) * (1 + 2.0 ** -20) + 1e-45
+            assert np.all(err <= bound), (t, b, err.max())
+
+
+def test_fp8_row_size_matches_hybridep_byte_counters():
+    g = json.load(open(os.path.join(GOLDEN, "hybridep_fp8_bytes.json")))
+    h = g["hidden"]
+    xb = W.f32_to_bf16_bits(np.ones((2, h), np.float32))
+    lay = oracle.layout(np.array([[0], [1]], np.int32), 2, 1, 1, 0)
+    q, sc = oracle.dispatch_fp8(xb, lay, 1, 1, False)
+    fp8_row = q.shape[1] * q.itemsize + sc.shape[1] * sc.itemsize
+    assert fp8_row == 7168 + 56 * 4
+    ratio = fp8_row / (h * 2)
+    printed = g["fp8_dispatch_nvl_recv_MB"] / g["bf16_combine_send_MB"]
+    assert abs(ratio - printed) < 1e-3
+
+
+# ---------------------------------------------------------------- bf16 dispatch
+@pytest.mark.parametrize("relay", [False, True])
+def test_dispatch_bf16_rows_are_token_rows(relay):
+    w = W.WORKLOADS["tiny"]
+    d = W.make_inputs(w)
+    lay = oracle.layout(d["topk_idx"], w.num_experts, w.num_ranks, w.num_hosts, 0, relay=relay)
+    recv = oracle.dispatch_bf16(d["x"], lay, w.topk, w.num_hosts, relay)
+    if relay:
+        assert recv.shape[0] == lay["host_tokens"].sum()
+        assert np.array_equal(recv, d["x"][lay["relay_token"][:recv.shape[0]]])
+    else:
+        assert recv.shape[0] == w.num_tokens * w.topk
+        assert np.array_equal(recv, d["x"][lay["row_token"]])
+
+
+# ---------------------------------------------------------------- combine
+def _combine_case(T=40, k=4, E=16, hidden=256, seed=9):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    idx = W.draw_routing(rng, T, E, k, "uniform")
+    w = W.draw_gate_weights(rng, T, k)
+    lay = oracle.layout(idx, E, 4, 2, 0)
+    y = W.f32_to_bf16_bits(rng.standard_normal((T * k, hidden), dtype=np.float32) * 3)
+    return idx, w, lay, y
+
+
+def test_combine_within_float32_bound_of_float64_sum():
+    idx, w, lay, y = _combine_case()
+    T, k = w.shape
+    out = W.bf16_bits_to_f32(oracle.combine(y, lay, w)).astype(np.float64)
+    yf = W.bf16_bits_to_f32(y).astype(np.float64)
+    terms = w.astype(np.float64)[:, :, None] * yf[lay["slot"].reshape(T, k)]
+    exact = terms.sum(1)
+    gamma = k * 2.0 ** -24 / (1 - k * 2.0 ** -24)
+    bound = gamma * np.abs(terms).sum(1) * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(exact) + 1e-40
+    assert np.all(np.abs(out - exact) <= bound)
+    # and the stated tolerance against the float64 result rounded to bf16
+    ref = W.bf16_bits_to_f32(W.f32_to_bf16_bits(exact.astype(np.float32))).astype(np.float64)
+    assert np.all(np.abs(out - ref) <= 1e-2 + 4e-3 * np.abs(ref))
+
+
+def test_combine_exact_special_cases():
+    idx, w, lay, y = _combine_case()
+    T, k = w.shape
+    slot = lay["slot"].reshape(T, k)
+    # one-hot weights: an exact copy of the chosen expert's row
+    pick = np.arange(T) % k
+    oh = np.zeros_like(w)
+    oh[np.arange(T), pick] = 1.0
+    out = oracle.combine(y, lay, oh)
+    assert np.array_equal(out, y[slot[np.arange(T), pick]])
+    # k = 1, weight 1
+    lay1 = oracle.layout(idx[:, :1].copy(), 16, 4, 2, 0)
+    y1 = y[:T]
+    out1 = oracle.combine(y1, lay1, np.ones((T, 1), np.float32))
+    assert np.array_equal(out1, y1[lay1["slot"]])
+    # negative weights flip the sign exactly
+    out2 = oracle.combine(y1, lay1, -np.ones((T, 1), np.float32))
+    assert np.array_equal(out2, y1[lay1["slot"]] ^ np.uint16(0x8000))
+
+
+def test_combine_identity_experts_return_x():
+    """Experts that return their input, with weights summing to ~1: the
+    combine gives x back within one bf16 ulp."""
+    w = W.WORKLOADS["tiny"]
+    d = W.make_inputs(w)
+    lay = oracle.layout(d["topk_idx"], w.num_experts, w.num_ranks, w.num_hosts, 0)
+    recv = oracle.dispatch_bf16(d["x"], lay, w.topk, w.num_hosts, False)
+    out = oracle.combine(recv, lay, d["topk_weights"])
+    xf = W.bf16_bits_to_f32(d["x"]).astype(np.float64)
+    of = W.bf16_bits_to_f32(out).astype(np.float64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(xf) + 1e-30)[1] - 8)
+    assert np.all(np.abs(of - xf) <= ulp)
+
+
+def test_combine_config_rule_closed_form():
+    """With expert outputs y = x (1 + e/16), out ~ x * sum_j w_j (1 + e_j/16)."""
+    w = W.WORKLOADS["tiny"]
+    d = W.make_inputs(w)
+    lay = oracle.layout(d["topk_idx"], w.num_experts, w.num_ranks, w.num_hosts, 0)
+    recv = oracle.dispatch_bf16(d["x"], lay, w.topk, w.num_hosts, False)
+    e_rows = oracle.expert_of_rows(lay)
+    y = W.f32_to_bf16_bits(W.bf16_bits_to_f32(recv) * (1 + e_rows / 16.0).astype(np.float32)[:, None])
+    out = W.bf16_bits_to_f32(oracle.combine(y, lay, d["topk_weights"])).astype(np.float64)
+    xf = W.bf16_bits_to_f32(d["x"]).astype(np.float64)
+    fac = (d["topk_weights"].astype(np.float64) * (1 + d["topk_idx"] / 16.0)).sum(1)
+    exact = xf * fac[:, None]
+    mag = np.abs(xf) * (np.abs(d["topk_weights"]) * (1 + d["topk_idx"] / 16.0)).sum(1)[:, None]
+    assert np.all(np.abs(out - exact) <= 2.0 ** -7 * mag + 1e-30)
