@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark: one MoE layer's dispatch + combine on one MI355X.
+
+A step is one pass of the whole hot path over one batch: layout (routing ->
+counts, offsets, rows), dispatch (token rows -> per-expert or relay rows,
+bf16 or fp8) and combine (k expert outputs per token -> weighted bf16 sum).
+The expert computation between dispatch and combine is outside the path; its
+outputs are a fixed synthetic bf16 tensor resident in HBM.
+
+Default workload: 4096 tokens, hidden 7168, 256 experts, top-8 uniform, 16
+ranks on 2 hosts, per-expert mode, bf16. Inputs are resident in HBM before
+timing starts. Prints one JSON line.
+
+Timing: W warm-up steps, then K steps bracketed by torch.cuda.synchronize();
+HIP events on the launch stream around each kernel group give per-kernel
+averages. `value` is algorithmic bytes of the layer / time per layer.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, public specification
+
+
+def algorithmic_bytes(T, k, H, hidden, rows, relay, fp8):
+    """Bytes each kernel must move at minimum (each byte once, at DRAM).
+
+    dispatch: read x (T*h*2) and each token's destinations (T*D*4, D = k
+              slots or H relay slots); write the rows (rows*h*2 for bf16, or
+              rows*(h + h/128*4) for fp8 codes + float32 scales).
+    combine:  read the T*k expert rows (T*k*h*2), slots and weights
+              (T*k*8); write out (T*h*2).
+    layout:   read topk_idx twice (count and assign passes, 2*T*k*4); write
+              slot and row_token (2*T*k*4); relay mode also writes relay_slot
+              (T*H*4) and relay_token, fan-out and mask for every relay row
+              up to the capacity (cap*(k+2)*4).
+    """
+    D = H if relay else k
+    row_bytes = hidden + (hidden // 128) * 4 if fp8 else hidden * 2
+    dispatch = T * hidden * 2 + T * D * 4 + rows * row_bytes
+    combine = T * k * hidden * 2 + T * k * 8 + T * hidden * 2
+    layout = 4 * T * k * 4
+    if relay:
+        layout += T * H * 4 + T * min(k, H) * (k + 2) * 4
+    return {"dispatch": dispatch, "combine": combine, "layout": layout}
+
+
+def kernel_sources_hash():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "combine_epx_get_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_counter_traffic(kernel: str, workload: str):
+    """HBM traffic per launch from a committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("sources_hash") != kernel_sources_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, d, min_seconds=12.0, max_reps=64):
+    """The oracle as it stands (single-threaded C loops) on full layers of the
+    same workload: layout + per-expert bf16 dispatch + combine, repeated until
+    about min_seconds of CPU time have been spent. Returns (seconds per
+    layer, layers timed)."""
+    import oracle
+    T, k = d["topk_idx"].shape
+    y_np = None
+    reps, t_total = 0, 0.0
+    while reps < max_reps and (t_total < min_seconds or reps < 2):
+        t0 = time.perf_counter()
+        lay = oracle.layout(d["topk_idx"], w.num_experts, w.num_ranks, w.num_hosts, w.my_rank)
+        recv = oracle.dispatch_bf16(d["x"], lay, k, w.num_hosts, False)
+        y_np = recv if y_np is None else y_np
+        oracle.combine(y_np, lay, d["topk_weights"])
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return t_total / reps, reps
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="large_batch")
+    ap.add_argument("--mode", choices=["per_expert", "relay"], default=None)
+    ap.add_argument("--dtype", choices=["bf16", "fp8"], default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time spent timing the oracle for the baseline (0: skip)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path has no "
+              f"multi-GPU transport: every GPU would run the same independent single-rank layer).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from combine_epx_get_amd import epx
+    from combine_epx_get_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    mode = args.mode or w.modes[0]
+    dtype = args.dtype or w.dtypes[0]
+    relay = mode == "relay"
+    fp8 = dtype == "fp8"
+    torch.cuda.set_device(0)
+    dev = "cuda"
+
+    d = W.make_inputs(w)
+    T, k, hidden = d["T"], w.topk, w.hidden
+    p = epx.make_problem(T, k, w.num_experts, w.num_ranks, w.num_hosts, w.my_rank,
+                         epx.MODE_HOST_RELAY if relay else epx.MODE_PER_EXPERT)
+    L = epx.Layout(p, dev)
+    idx = torch.from_numpy(d["topk_idx"]).to(dev)
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    wts = torch.from_numpy(d["topk_weights"]).to(dev)
+    cap = epx.relay_capacity(p) if relay else T * k
+    if fp8:
+        recv = torch.empty((cap, hidden), dtype=torch.uint8, device=dev)
+        scales = torch.empty((cap, hidden // 128), dtype=torch.float32, device=dev)
+    else:
+        recv = torch.empty((cap, hidden), dtype=torch.bfloat16, device=dev)
+        scales = None
+    y = torch.from_numpy(W.random_bf16((T * k, hidden), seed=1000 + w.seed).view(np.int16)).view(torch.bfloat16).to(dev)
+    out = torch.empty((T, hidden), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    out_dtype = epx.FP8_E4M3 if fp8 else epx.BF16
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        epx.epx_get_layout(p, idx, L, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        epx.epx_dispatch(p, L, x, out_dtype, recv, scales, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        epx.epx_combine(p, L, y, wts, out, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert epx.epx_read_error(L) == 0
+    totals = L["totals"].cpu().numpy()
+    rows = int(totals[1] if relay else totals[0])
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    lay_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dis_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    com_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    ms_per_step = wall * 1e3 / args.steps
+
+    nbytes = algorithmic_bytes(T, k, w.num_hosts, hidden, rows, relay, fp8)
+    layer_bytes = sum(nbytes.values())
+    us_layer = float(step_ms.mean() * 1e3)
+    value = layer_bytes / (ms_per_step * 1e-3) / 1e9
+
+    per_kernel = {
+        "layout": {"us": float(lay_ms.mean() * 1e3), "bytes": nbytes["layout"]},
+        "dispatch": {"us": float(dis_ms.mean() * 1e3), "bytes": nbytes["dispatch"]},
+        "combine": {"us": float(com_ms.mean() * 1e3), "bytes": nbytes["combine"]},
+    }
+    for v in per_kernel.values():
+        v["GBs"] = v["bytes"] / (v["us"] * 1e-6) / 1e9
+        v["frac_peak"] = v["GBs"] / PEAK_HBM_GBS
+    dom = max(("dispatch", "combine"), key=lambda n: per_kernel[n]["us"])
+    kname = {"dispatch": "dispatch_fp8_kernel" if fp8 else "dispatch_bf16_kernel",
+             "combine": "combine_kernel"}[dom]
+    traffic = load_counter_traffic(kname, args.workload)
+    roofline = {"bound": "hbm", "kernel": kname,
+                "achieved": round(per_kernel[dom]["GBs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(per_kernel[dom]["frac_peak"], 4), "traffic": traffic,
+                "algorithmic_bytes": per_kernel[dom]["bytes"]}
+
+    cpu = None
+    if args.cpu_seconds > 0 and not relay and not fp8:
+        cpu_s, reps = cpu_baseline(w, d, args.cpu_seconds)
+        cpu = {"value": round(layer_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "us_per_layer": round(cpu_s * 1e6, 1),
+               "sample": f"{reps} full layers (layout + per-expert bf16 dispatch + combine) of the "
+                         f"{args.workload} workload, single-threaded C oracle"}
+
+    line = {
+        "metric": "dispatch+combine µs/layer and HBM GB/s (% of MI355X peak) at 4096 tok, h=7168",
+        "value": round(value, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if not fp8 else "fp8-e4m3 dispatch / bf16 combine",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "hidden": hidden, "experts": w.num_experts,
+                   "topk": k, "ranks": w.num_ranks, "hosts": w.num_hosts, "routing": w.routing,
+                   "mode": mode, "payload": dtype},
+        "us_per_layer": round(us_layer, 2),
+        "pct_of_peak_layer": round(100 * layer_bytes / (us_layer * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+        "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for n, v in per_kernel.items()},
+        "layer_bytes": layer_bytes, "rows": rows,
+        "imbalance_ratio": round(float(totals[2]) / (T * k / w.num_experts), 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,219 @@
+// epx_api.hip -- the C ABI of libepx: argument checks, sizes and launches.
+// Every check here runs on the host before anything is launched; a call that
+// fails a check launches nothing.
+#include <stdint.h>
+
+#include "epx_internal.h"
+
+namespace {
+
+using epx::Geometry;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Validates the problem and fills the kernel geometry.
+epx_status make_geometry(const epx_problem *p, Geometry *g)
+{
+    if (!p)
+        return EPX_ERR_ARG;
+    const int32_t T = p->num_tokens, k = p->topk, E = p->num_experts, R = p->num_ranks,
+                  H = p->num_hosts, s = p->my_rank;
+    if (T < 0 || T > (1 << 24) || k < 1 || k > epx::kMaxTopk || E < 1 || E > epx::kMaxExperts)
+        return EPX_ERR_ARG;
+    if (R < 1 || H < 1 || H > epx::kMaxHosts || E % R != 0 || R % H != 0 || k > E)
+        return EPX_ERR_ARG;
+    if (R / H > epx::kMaxRanksPerHost || s < 0 || s >= R)
+        return EPX_ERR_ARG;
+    if (p->mode != EPX_MODE_PER_EXPERT && p->mode != EPX_MODE_HOST_RELAY)
+        return EPX_ERR_ARG;
+    if ((int64_t)T * k >= ((int64_t)1 << 31))
+        return EPX_ERR_ARG;
+    g->T = T;
+    g->k = k;
+    g->E = E;
+    g->R = R;
+    g->H = H;
+    g->s = s;
+    g->epr = E / R;
+    g->rph = R / H;
+    g->G = T > 0 ? (T + epx::kChunkTokens - 1) / epx::kChunkTokens : 1;
+    int nbits = 0;
+    while ((1 << nbits) < E)
+        ++nbits;
+    g->nbits = nbits;
+    g->relay = p->mode == EPX_MODE_HOST_RELAY;
+    return EPX_OK;
+}
+
+int64_t relay_capacity(const Geometry &g) { return (int64_t)g.T * (g.k < g.H ? g.k : g.H); }
+
+void sizes_of(const Geometry &g, int64_t s[EPX_LAYOUT_NARRAYS])
+{
+    const int64_t cap = relay_capacity(g);
+    s[EPX_L_EXPERT_COUNT] = g.E;
+    s[EPX_L_EXPERT_OFFSET] = g.E + 1;
+    s[EPX_L_RANK_ROWS] = g.R;
+    s[EPX_L_RANK_TOKENS] = g.R;
+    s[EPX_L_RANK_OFFSET] = g.R + 1;
+    s[EPX_L_HOST_TOKENS] = g.H;
+    s[EPX_L_HOST_OFFSET] = g.H + 1;
+    s[EPX_L_SLOT] = (int64_t)g.T * g.k;
+    s[EPX_L_ROW_TOKEN] = (int64_t)g.T * g.k;
+    s[EPX_L_RELAY_SLOT] = (int64_t)g.T * g.H;
+    s[EPX_L_RELAY_TOKEN] = cap;
+    s[EPX_L_FANOUT_EXPERT] = cap * g.k;
+    s[EPX_L_FANOUT_RANK_MASK] = cap;
+    s[EPX_L_RELAY_DST_RANK] = g.H;
+    s[EPX_L_TOTALS] = 4;
+    s[EPX_L_WORKSPACE] = (int64_t)g.G * (g.E + g.R + g.H + 1);
+}
+
+// Every array the layout kernels write must be present (relay arrays only in
+// relay mode) and 4-byte aligned.
+epx_status check_layout(const Geometry &g, const epx_layout *L)
+{
+    if (!L)
+        return EPX_ERR_ARG;
+    const void *need[] = {L->expert_count, L->expert_offset, L->rank_rows, L->rank_tokens,
+                          L->rank_offset, L->host_tokens, L->host_offset, L->slot,
+                          L->row_token, L->relay_dst_rank, L->totals, L->workspace};
+    for (const void *q : need)
+        if (!q || !aligned(q, 4))
+            return EPX_ERR_ARG;
+    if (g.relay) {
+        const void *rel[] = {L->relay_slot, L->relay_token, L->fanout_expert, L->fanout_rank_mask};
+        for (const void *q : rel)
+            if (!q || !aligned(q, 4))
+                return EPX_ERR_ARG;
+    }
+    return EPX_OK;
+}
+
+epx_status from_hip(hipError_t e) { return e == hipSuccess ? EPX_OK : EPX_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t epx_abi_version(void) { return EPX_ABI_VERSION; }
+
+const char *epx_status_string(epx_status s)
+{
+    switch (s) {
+    case EPX_OK:
+        return "ok";
+    case EPX_ERR_ARG:
+        return "invalid argument (pointer, alignment, geometry or size)";
+    case EPX_ERR_INDEX:
+        return "expert id out of range in topk_idx";
+    case EPX_ERR_CAPACITY:
+        return "output buffer smaller than required";
+    case EPX_ERR_DEVICE:
+        return "HIP launch or runtime failure";
+    }
+    return "unknown status";
+}
+
+epx_status epx_layout_sizes(const epx_problem *p, int64_t sizes_out[EPX_LAYOUT_NARRAYS])
+{
+    Geometry g;
+    epx_status st = make_geometry(p, &g);
+    if (st != EPX_OK)
+        return st;
+    if (!sizes_out)
+        return EPX_ERR_ARG;
+    sizes_of(g, sizes_out);
+    return EPX_OK;
+}
+
+epx_status epx_get_layout(const epx_problem *p, const int32_t *topk_idx, const epx_layout *layout,
+                          void *stream)
+{
+    Geometry g;
+    epx_status st = make_geometry(p, &g);
+    if (st != EPX_OK)
+        return st;
+    if ((st = check_layout(g, layout)) != EPX_OK)
+        return st;
+    if (g.T > 0 && (!topk_idx || !aligned(topk_idx, 4)))
+        return EPX_ERR_ARG;
+    return from_hip(epx::launch_layout(g, topk_idx, *layout, (hipStream_t)stream));
+}
+
+epx_status epx_dispatch(const epx_problem *p, const epx_layout *layout, const void *x,
+                        int32_t hidden, int32_t out_dtype, void *recv, float *recv_scales,
+                        int64_t capacity_rows, void *stream)
+{
+    Geometry g;
+    epx_status st = make_geometry(p, &g);
+    if (st != EPX_OK)
+        return st;
+    if ((st = check_layout(g, layout)) != EPX_OK)
+        return st;
+    if (out_dtype != EPX_BF16 && out_dtype != EPX_FP8_E4M3)
+        return EPX_ERR_ARG;
+    if (hidden < 8 || hidden % 8 != 0 || (out_dtype == EPX_FP8_E4M3 && hidden % epx::kFp8Block != 0))
+        return EPX_ERR_ARG;
+    const int64_t need = g.relay ? relay_capacity(g) : (int64_t)g.T * g.k;
+    if (capacity_rows < need)
+        return EPX_ERR_CAPACITY;
+    if (g.T == 0)
+        return EPX_OK;   // nothing to move; the activation pointers are not used
+    if (!x || !recv || !aligned(x, 16) || !aligned(recv, 16))
+        return EPX_ERR_ARG;
+    if (out_dtype == EPX_FP8_E4M3 && (!recv_scales || !aligned(recv_scales, 4)))
+        return EPX_ERR_ARG;
+    const hipStream_t s = (hipStream_t)stream;
+    if (out_dtype == EPX_BF16)
+        return from_hip(epx::launch_dispatch_bf16(g, *layout, x, hidden, recv, s));
+    return from_hip(epx::launch_dispatch_fp8(g, *layout, x, hidden, recv, recv_scales, s));
+}
+
+epx_status epx_combine(const epx_problem *p, const epx_layout *layout, const void *y,
+                       int64_t y_rows, const float *topk_weights, int32_t hidden, void *out,
+                       void *stream)
+{
+    Geometry g;
+    epx_status st = make_geometry(p, &g);
+    if (st != EPX_OK)
+        return st;
+    if ((st = check_layout(g, layout)) != EPX_OK)
+        return st;
+    if (hidden < 8 || hidden % 8 != 0)
+        return EPX_ERR_ARG;
+    if (y_rows < (int64_t)g.T * g.k)
+        return EPX_ERR_CAPACITY;
+    if (g.T == 0)
+        return EPX_OK;
+    if (!y || !out || !topk_weights || !aligned(y, 16) || !aligned(out, 16) ||
+        !aligned(topk_weights, 4))
+        return EPX_ERR_ARG;
+    return from_hip(
+        epx::launch_combine(g, *layout, y, topk_weights, hidden, out, (hipStream_t)stream));
+}
+
+epx_status epx_read_error(const epx_layout *layout, int32_t *bad_count, void *stream)
+{
+    if (!layout || !layout->totals)
+        return EPX_ERR_ARG;
+    int32_t totals[4];
+    const hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(totals, layout->totals, sizeof totals, hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return EPX_ERR_DEVICE;
+    if (bad_count)
+        *bad_count = totals[3];
+    return totals[3] == 0 ? EPX_OK : EPX_ERR_INDEX;
+}
+
+epx_status epx_f32_to_e4m3(const float *in, uint8_t *out, int64_t n, void *stream)
+{
+    if (n < 0 || (n > 0 && (!in || !out || !aligned(in, 4))))
+        return EPX_ERR_ARG;
+    if (n == 0)
+        return EPX_OK;
+    return from_hip(epx::launch_f32_to_e4m3(in, out, n, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+"""Thin ctypes binding over libepx.so (the C ABI in include/epx.h).
+
+Argument marshalling only: tensors are checked for dtype, shape, device and
+contiguity, and their data pointers and the current HIP stream are passed to
+the library. Every step of dispatch and combine runs in the library's HIP
+kernels; there is no fallback of any kind. Importing this module fails when
+the library has not been built (``python -m combine_epx_get_amd.build``).
+
+PyTorch serves as the device allocator and stream provider only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libepx.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is not built; run `python -m combine_epx_get_amd.build`")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+MODE_PER_EXPERT = 0
+MODE_HOST_RELAY = 1
+BF16 = 0
+FP8_E4M3 = 1
+
+STATUS = {0: "EPX_OK", 1: "EPX_ERR_ARG", 2: "EPX_ERR_INDEX", 3: "EPX_ERR_CAPACITY", 4: "EPX_ERR_DEVICE"}
+
+LAYOUT_FIELDS = ["expert_count", "expert_offset", "rank_rows", "rank_tokens", "rank_offset",
+                 "host_tokens", "host_offset", "slot", "row_token", "relay_slot", "relay_token",
+                 "fanout_expert", "fanout_rank_mask", "relay_dst_rank", "totals", "workspace"]
+RELAY_FIELDS = ("relay_slot", "relay_token", "fanout_expert", "fanout_rank_mask")
+
+
+class epx_problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("num_tokens", "topk", "num_experts", "num_ranks", "num_hosts", "my_rank", "mode")]
+
+
+class epx_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYOUT_FIELDS]
+
+
+_P = ctypes.c_void_p
+_lib.epx_layout_sizes.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(ctypes.c_int64)]
+_lib.epx_get_layout.argtypes = [ctypes.POINTER(epx_problem), _P, ctypes.POINTER(epx_layout), _P]
+_lib.epx_dispatch.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_layout), _P,
+                              ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int64, _P]
+_lib.epx_combine.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_layout), _P,
+                             ctypes.c_int64, _P, ctypes.c_int32, _P, _P]
+_lib.epx_read_error.argtypes = [ctypes.POINTER(epx_layout), ctypes.POINTER(ctypes.c_int32), _P]
+_lib.epx_f32_to_e4m3.argtypes = [_P, _P, ctypes.c_int64, _P]
+_lib.epx_status_string.argtypes = [ctypes.c_int]
+_lib.epx_status_string.restype = ctypes.c_char_p
+for _f in ("epx_layout_sizes", "epx_get_layout", "epx_dispatch", "epx_combine", "epx_read_error",
+           "epx_f32_to_e4m3"):
+    getattr(_lib, _f).restype = ctypes.c_int
+_lib.epx_abi_version.restype = ctypes.c_int32
+NARRAYS = len(LAYOUT_FIELDS)
+
+
+class EpxError(RuntimeError):
+    def __init__(self, code: int, call: str):
+        msg = _lib.epx_status_string(code).decode()
+        super().__init__(f"{call}: {STATUS.get(code, code)} ({msg})")
+        self.code = code
+
+
+def _check(code: int, call: str) -> None:
+    if code != 0:
+        raise EpxError(code, call)
+
+
+def abi_version() -> int:
+    return int(_lib.epx_abi_version())
+
+
+def make_problem(num_tokens: int, topk: int, num_experts: int, num_ranks: int, num_hosts: int,
+                 my_rank: int = 0, mode: int = MODE_PER_EXPERT) -> epx_problem:
+    return epx_problem(num_tokens, topk, num_experts, num_ranks, num_hosts, my_rank, mode)
+
+
+def epx_layout_sizes(problem: epx_problem) -> List[int]:
+    sizes = (ctypes.c_int64 * NARRAYS)()
+    _check(_lib.epx_layout_sizes(ctypes.byref(problem), sizes), "epx_layout_sizes")
+    return list(sizes)
+
+
+class Layout:
+    """Device arrays of one layout (torch tensors) and the matching C struct."""
+
+    def __init__(self, problem: epx_problem, device="cuda"):
+        sizes = epx_layout_sizes(problem)
+        relay = problem.mode == MODE_HOST_RELAY
+        self.problem = problem
+        self.tensors: Dict[str, torch.Tensor] = {}
+        ptrs = []
+        for name, n in zip(LAYOUT_FIELDS, sizes):
+            if name in RELAY_FIELDS and not relay:
+                ptrs.append(None)
+                continue
+            t = torch.empty(max(int(n), 1), dtype=torch.int32, device=device)
+            self.tensors[name] = t
+            ptrs.append(t.data_ptr())
+        self.struct = epx_layout(*ptrs)
+        self.sizes = dict(zip(LAYOUT_FIELDS, sizes))
+
+    def __getitem__(self, name: str) -> torch.Tensor:
+        return self.tensors[name][: self.sizes[name]]
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str, ndim: Optional[int] = None) -> None:
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: need a contiguous {dtype} CUDA tensor")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: need {ndim} dimensions, got {tuple(t.shape)}")
+
+
+def epx_get_layout(problem: epx_problem, topk_idx: torch.Tensor, layout: Layout, stream=None) -> None:
+    _need(topk_idx, torch.int32, "topk_idx", 2)
+    if tuple(topk_idx.shape) != (problem.num_tokens, problem.topk):
+        raise ValueError(f"topk_idx shape {tuple(topk_idx.shape)} != (T, k)")
+    _check(_lib.epx_get_layout(ctypes.byref(problem), topk_idx.data_ptr(), ctypes.byref(layout.struct),
+                               _stream(stream)), "epx_get_layout")
+
+
+def epx_dispatch(problem: epx_problem, layout: Layout, x: torch.Tensor, out_dtype: int,
+                 recv: torch.Tensor, recv_scales: Optional[torch.Tensor] = None, stream=None) -> None:
+    _need(x, torch.bfloat16, "x", 2)
+    if x.shape[0] != problem.num_tokens:
+        raise ValueError("x: first dimension must be num_tokens")
+    hidden = x.shape[1]
+    if out_dtype == BF16:
+        _need(recv, torch.bfloat16, "recv", 2)
+        scales_ptr = None
+    else:
+        _need(recv, torch.uint8, "recv", 2)
+        _need(recv_scales, torch.float32, "recv_scales", 2)
+        if recv_scales.shape != (recv.shape[0], hidden // 128):
+            raise ValueError("recv_scales: need [capacity_rows, hidden/128]")
+        scales_ptr = recv_scales.data_ptr()
+    if recv.shape[1] != hidden:
+        raise ValueError("recv: second dimension must be hidden")
+    _check(_lib.epx_dispatch(ctypes.byref(problem), ctypes.byref(layout.struct), x.data_ptr(), hidden,
+                             out_dtype, recv.data_ptr(), scales_ptr, recv.shape[0], _stream(stream)),
+           "epx_dispatch")
+
+
+def epx_combine(problem: epx_problem, layout: Layout, y: torch.Tensor, topk_weights: torch.Tensor,
+                out: torch.Tensor, stream=None) -> None:
+    _need(y, torch.bfloat16, "y", 2)
+    _need(topk_weights, torch.float32, "topk_weights", 2)
+    _need(out, torch.bfloat16, "out", 2)
+    if tuple(topk_weights.shape) != (problem.num_tokens, problem.topk):
+        raise ValueError("topk_weights: need [T, k]")
+    if tuple(out.shape) != (problem.num_tokens, y.shape[1]):
+        raise ValueError("out: need [T, hidden]")
+    _check(_lib.epx_combine(ctypes.byref(problem), ctypes.byref(layout.struct), y.data_ptr(), y.shape[0],
+                            topk_weights.data_ptr(), y.shape[1], out.data_ptr(), _stream(stream)),
+           "epx_combine")
+
+
+def epx_read_error(layout: Layout, stream=None) -> int:
+    """Synchronising read of the layout's bad-id count (0 = all ids valid)."""
+    bad = ctypes.c_int32(0)
+    code = _lib.epx_read_error(ctypes.byref(layout.struct), ctypes.byref(bad), _stream(stream))
+    if code not in (0, 2):
+        _check(code, "epx_read_error")
+    return int(bad.value)
+
+
+def epx_f32_to_e4m3(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    _need(inp, torch.float32, "in")
+    _need(out, torch.uint8, "out")
+    if inp.numel() != out.numel():
+        raise ValueError("in/out sizes differ")
+    _check(_lib.epx_f32_to_e4m3(inp.data_ptr(), out.data_ptr(), inp.numel(), _stream(stream)),
+           "epx_f32_to_e4m3")
+
+
+def relay_capacity(problem: epx_problem) -> int:
+    return problem.num_tokens * min(problem.topk, problem.num_hosts)

@@ -1,0 +1,184 @@
+/*
+ * epx.h -- C ABI of the MI355X (gfx950) MoE expert-parallel dispatch/combine
+ * library (libepx.so).
+ *
+ * The operations follow "Balancing and Beyond: Communication-Centric
+ * Optimizations in Expert Parallelism" (research digest) and the DeepEP
+ * issues "[GH-ISSUE #250] Profiling when rank unbalance" and "Poor HybridEP
+ * performance on dual-node 16x B300 GPUs". One call sequence serves one
+ * source rank of an expert-parallel group on one GPU:
+ *
+ *   epx_get_layout   -- top-k routing -> counts, offsets and row positions
+ *   epx_dispatch     -- token rows -> per-expert rows (Mode 1) or one row per
+ *                       destination host (Mode 2 relay), bf16 or fp8
+ *   epx_combine      -- k expert outputs per token -> weighted sum, bf16
+ *
+ * Conventions for every call:
+ *  - Every array argument is a DEVICE pointer the caller allocated; the
+ *    library allocates nothing, frees nothing and keeps no global state.
+ *    Activation pointers (x, recv, y, out) must be 16-byte aligned.
+ *  - Calls are asynchronous and ordered on the HIP stream passed as `stream`
+ *    (a hipStream_t; NULL = the null stream). No call synchronises the host,
+ *    except epx_read_error.
+ *  - Host-side argument checks fail with EPX_ERR_ARG or EPX_ERR_CAPACITY and
+ *    then launch nothing. A failed kernel launch returns EPX_ERR_DEVICE.
+ *  - An expert id outside [0, num_experts) is a device-side error: the
+ *    layout counts such ids into totals[3]; dispatch and combine then write
+ *    nothing; epx_read_error reports EPX_ERR_INDEX.
+ *  - Supported sizes: 1 <= topk <= 64, topk <= num_experts <= 2048,
+ *    num_experts % num_ranks == 0, num_ranks % num_hosts == 0,
+ *    num_hosts <= 64, ranks per host <= 32, 0 <= my_rank < num_ranks,
+ *    0 <= num_tokens <= 2^24 and num_tokens * topk < 2^31.
+ */
+#ifndef EPX_H
+#define EPX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EPX_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define EPX_API __attribute__((visibility("default")))
+#else
+#define EPX_API
+#endif
+
+typedef enum {
+    EPX_OK = 0,
+    EPX_ERR_ARG = 1,      /* bad pointer, alignment, geometry or size     */
+    EPX_ERR_INDEX = 2,    /* an expert id out of range (device-detected)  */
+    EPX_ERR_CAPACITY = 3, /* an output buffer smaller than required       */
+    EPX_ERR_DEVICE = 4    /* a HIP launch or runtime call failed          */
+} epx_status;
+
+/* Transport layout of dispatch (digest section 3.2, Figure 3).
+ * PER_EXPERT: one copy of a token per destination expert (DeepEP's Mode 1).
+ * HOST_RELAY: one copy per destination host, addressed to the same-index GPU
+ *             on that host, plus an index to fan it out there (Mode 2 with
+ *             de-redundancy). */
+typedef enum { EPX_MODE_PER_EXPERT = 0, EPX_MODE_HOST_RELAY = 1 } epx_mode;
+
+/* Dispatch payload. FP8_E4M3: OCP E4M3FN codes with one float32 scale per
+ * 128 channels (the BF16-to-FP8 conversion inside dispatch, digest section
+ * 3.1). */
+typedef enum { EPX_BF16 = 0, EPX_FP8_E4M3 = 1 } epx_dtype;
+
+/* The problem of one source rank. Experts sit on ranks in contiguous
+ * blocks (rank(e) = e / (num_experts/num_ranks)), ranks on hosts in
+ * contiguous blocks (host(r) = r / (num_ranks/num_hosts)). */
+typedef struct {
+    int32_t num_tokens;   /* T: tokens of this source rank           */
+    int32_t topk;         /* k: experts per token                     */
+    int32_t num_experts;  /* E                                        */
+    int32_t num_ranks;    /* R: expert-parallel ranks                 */
+    int32_t num_hosts;    /* H: hosts the ranks are spread over       */
+    int32_t my_rank;      /* s: this source rank                      */
+    int32_t mode;         /* epx_mode                                 */
+} epx_problem;
+
+/* Index of each layout array in the sizes reported by epx_layout_sizes. */
+enum {
+    EPX_L_EXPERT_COUNT = 0,  /* int32 [E]    copies per expert                                */
+    EPX_L_EXPERT_OFFSET,     /* int32 [E+1]  exclusive prefix of expert_count                 */
+    EPX_L_RANK_ROWS,         /* int32 [R]    copies per rank (sum over its experts)           */
+    EPX_L_RANK_TOKENS,       /* int32 [R]    tokens with >= 1 expert on the rank              */
+    EPX_L_RANK_OFFSET,       /* int32 [R+1]  = expert_offset[r * E/R]                         */
+    EPX_L_HOST_TOKENS,       /* int32 [H]    tokens with >= 1 expert on the host (relay rows) */
+    EPX_L_HOST_OFFSET,       /* int32 [H+1]  exclusive prefix of host_tokens                  */
+    EPX_L_SLOT,              /* int32 [T*k]  per-expert row of pair (t, j)                    */
+    EPX_L_ROW_TOKEN,         /* int32 [T*k]  source token of each per-expert row              */
+    EPX_L_RELAY_SLOT,        /* int32 [T*H]  relay row of (t, h), -1 if t has no expert on h  */
+    EPX_L_RELAY_TOKEN,       /* int32 [C]    source token of each relay row, -1 past the end  */
+    EPX_L_FANOUT_EXPERT,     /* int32 [C*k]  expert j of the row's token if on the row's host */
+    EPX_L_FANOUT_RANK_MASK,  /* uint32 [C]   bit (rank mod R/H) for each local rank to feed   */
+    EPX_L_RELAY_DST_RANK,    /* int32 [H]    same-index GPU: h*(R/H) + my_rank mod (R/H)     */
+    EPX_L_TOTALS,            /* int32 [4]    rows, relay rows, max expert count, bad ids      */
+    EPX_L_WORKSPACE,         /* int32 [..]   scratch between the layout kernels               */
+    EPX_LAYOUT_NARRAYS
+};
+
+/* Device arrays of one layout. Row order (the digest fixes none):
+ *  - per-expert rows: by expert, then token, then position j, so one
+ *    expert's rows keep token order and one rank's rows are contiguous;
+ *  - relay rows: by host, then token; a token's own host gets a row too.
+ * C = T * min(k, H) is the relay row capacity (batch x k sizing of the
+ * digest, section 3.4). The four relay arrays are written in HOST_RELAY mode
+ * only and may be NULL in PER_EXPERT mode. */
+typedef struct {
+    int32_t *expert_count;
+    int32_t *expert_offset;
+    int32_t *rank_rows;
+    int32_t *rank_tokens;
+    int32_t *rank_offset;
+    int32_t *host_tokens;
+    int32_t *host_offset;
+    int32_t *slot;
+    int32_t *row_token;
+    int32_t *relay_slot;
+    int32_t *relay_token;
+    int32_t *fanout_expert;
+    uint32_t *fanout_rank_mask;
+    int32_t *relay_dst_rank;
+    int32_t *totals;
+    int32_t *workspace;
+} epx_layout;
+
+/* Element counts (not bytes) of each layout array, indexed by EPX_L_*.
+ * Host only; returns EPX_ERR_ARG for an unsupported problem. */
+EPX_API epx_status epx_layout_sizes(const epx_problem *p, int64_t sizes_out[EPX_LAYOUT_NARRAYS]);
+
+/* Counts, offsets and row positions for topk_idx [T, k] (int32, row-major).
+ * The layout arrays are overwritten (no zeroing needed beforehand); the
+ * workspace is scratch owned by the caller for the duration of the call. */
+EPX_API epx_status epx_get_layout(const epx_problem *p, const int32_t *topk_idx,
+                          const epx_layout *layout, void *stream);
+
+/* Scatter token rows into the layout's destination rows.
+ *  x            bf16 [T, hidden], row-major
+ *  out_dtype    EPX_BF16: recv is bf16 [capacity_rows, hidden];
+ *               EPX_FP8_E4M3: recv is uint8 codes [capacity_rows, hidden] and
+ *               recv_scales float32 [capacity_rows, hidden/128], where for
+ *               token t and block b: scale = max|x[t, 128b:128b+128]| / 448
+ *               (float32 division) and code = E4M3(x / scale) rounded to
+ *               nearest even with saturation at +-448; an all-zero block has
+ *               scale 0 and codes +-0.
+ *  hidden       multiple of 8 (bf16) or of 128 (fp8)
+ *  capacity_rows >= T*k (PER_EXPERT) or >= T*min(k, H) (HOST_RELAY)
+ * Rows are written at the layout's slots (PER_EXPERT) or relay slots
+ * (HOST_RELAY); other rows of recv are left untouched. */
+EPX_API epx_status epx_dispatch(const epx_problem *p, const epx_layout *layout, const void *x,
+                        int32_t hidden, int32_t out_dtype, void *recv, float *recv_scales,
+                        int64_t capacity_rows, void *stream);
+
+/* out[t, :] = bf16( sum_j topk_weights[t, j] * y[slot[t, j], :] ): the k
+ * expert outputs of each token gathered from the per-expert rows of y
+ * (bf16 [y_rows, hidden], y_rows >= T*k) and summed in float32 as
+ * acc = fma(w, y, acc) for j = 0..k-1 from +0, rounded to bf16 (nearest
+ * even). Weights are used as given. hidden must be a multiple of 8. */
+EPX_API epx_status epx_combine(const epx_problem *p, const epx_layout *layout, const void *y,
+                       int64_t y_rows, const float *topk_weights, int32_t hidden, void *out,
+                       void *stream);
+
+/* Synchronises `stream`, then reads totals[3]: EPX_OK, or EPX_ERR_INDEX when
+ * the last layout on this layout's arrays saw out-of-range expert ids (their
+ * number in *bad_count if not NULL). For tests and debugging. */
+EPX_API epx_status epx_read_error(const epx_layout *layout, int32_t *bad_count, void *stream);
+
+/* Elementwise float32 -> E4M3FN with the rounding and saturation that the
+ * fp8 dispatch uses (in [n] -> out [n], device arrays). A diagnostic entry
+ * point for checking the conversion exhaustively. */
+EPX_API epx_status epx_f32_to_e4m3(const float *in, uint8_t *out, int64_t n, void *stream);
+
+EPX_API const char *epx_status_string(epx_status s);
+EPX_API int32_t epx_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EPX_H */
