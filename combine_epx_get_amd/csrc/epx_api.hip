@@ -36,7 +36,12 @@ epx_status make_geometry(const epx_problem *p, Geometry *g)
     g->s = s;
     g->epr = E / R;
     g->rph = R / H;
-    g->G = T > 0 ? (T + epx::kChunkTokens - 1) / epx::kChunkTokens : 1;
+    g->ct = k <= 16 ? 64 : epx::kChunkPairs / k;
+    g->G = T > 0 ? (T + g->ct - 1) / g->ct : 1;
+    g->Gs = (g->G + 3) & ~3;
+    g->div_epr.init(g->epr);
+    g->div_rph.init(g->rph);
+    g->div_k.init(k);
     int nbits = 0;
     while ((1 << nbits) < E)
         ++nbits;
@@ -65,7 +70,7 @@ void sizes_of(const Geometry &g, int64_t s[EPX_LAYOUT_NARRAYS])
     s[EPX_L_FANOUT_RANK_MASK] = cap;
     s[EPX_L_RELAY_DST_RANK] = g.H;
     s[EPX_L_TOTALS] = 4;
-    s[EPX_L_WORKSPACE] = (int64_t)g.G * (g.E + g.R + g.H + 1);
+    s[EPX_L_WORKSPACE] = (int64_t)(g.Gs + 1) * (g.E + g.R + g.H + 1);
 }
 
 // Every array the layout kernels write must be present (relay arrays only in
@@ -76,10 +81,12 @@ epx_status check_layout(const Geometry &g, const epx_layout *L)
         return EPX_ERR_ARG;
     const void *need[] = {L->expert_count, L->expert_offset, L->rank_rows, L->rank_tokens,
                           L->rank_offset, L->host_tokens, L->host_offset, L->slot,
-                          L->row_token, L->relay_dst_rank, L->totals, L->workspace};
+                          L->row_token, L->relay_dst_rank, L->totals};
     for (const void *q : need)
         if (!q || !aligned(q, 4))
             return EPX_ERR_ARG;
+    if (!L->workspace || !aligned(L->workspace, 16))
+        return EPX_ERR_ARG;
     if (g.relay) {
         const void *rel[] = {L->relay_slot, L->relay_token, L->fanout_expert, L->fanout_rank_mask};
         for (const void *q : rel)

@@ -8,17 +8,17 @@
 // once to bf16, nearest even: the same order on every element, so results
 // are deterministic and independent of the launch shape.
 //
-// One workgroup per token; each lane owns 8 channels (one 16-byte vector per
-// row). A lane issues the loads of up to 8 expert rows before its first FMA,
-// so 8 x 16 bytes per lane are in flight: an HBM-bound gather that reads
-// T*k*h*2 bytes and writes T*h*2.
+// One workgroup per (token, column slice); each lane owns 8 channels in each
+// of kChunks 16-byte chunks and issues the loads of up to 8 expert rows for
+// all its chunks before the first fma (16 x 16 bytes in flight per lane).
+// Reads T*k*h*2 bytes and writes T*h*2: an HBM-bound gather.
 #include "epx_internal.h"
 
 namespace epx {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBatch = 8;    // expert rows loaded before the FMAs
+constexpr int kBatch = 8;    // expert rows loaded before the fmas
+constexpr int kChunks = 2;   // 16-byte chunks per lane
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -32,8 +32,8 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f)
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-__global__ __launch_bounds__(kThreads) void combine_kernel(
-    const u32x4 *__restrict__ y, int nvec, const int32_t *__restrict__ slot,
+__global__ __launch_bounds__(1024) void combine_kernel(
+    const u32x4 *__restrict__ y, int nvec, int slice, const int32_t *__restrict__ slot,
     const float *__restrict__ w, int k, u32x4 *__restrict__ out,
     const int32_t *__restrict__ totals)
 {
@@ -42,43 +42,60 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     if (totals[3] != 0)
         return;   // the layout saw out-of-range expert ids
     const int64_t t = blockIdx.x;
+    const int c_beg = blockIdx.y * slice;
+    const int c_end = min(nvec, c_beg + slice);
     if (threadIdx.x < k) {
         s_row[threadIdx.x] = slot[t * k + threadIdx.x];
         s_w[threadIdx.x] = w[t * k + threadIdx.x];
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < nvec; c += kThreads) {
-        float acc[8];
+    for (int c0 = c_beg + threadIdx.x; c0 < c_end; c0 += blockDim.x * kChunks) {
+        float acc[kChunks][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            acc[i] = 0.0f;
+        for (int i = 0; i < kChunks; ++i)
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                acc[i][q] = 0.0f;
         for (int j0 = 0; j0 < k; j0 += kBatch) {
-            u32x4 v[kBatch];
+            u32x4 v[kChunks][kBatch];
 #pragma unroll
             for (int jj = 0; jj < kBatch; ++jj)
-                if (j0 + jj < k)
-                    v[jj] = __builtin_nontemporal_load(y + (int64_t)s_row[j0 + jj] * nvec + c);
+#pragma unroll
+                for (int i = 0; i < kChunks; ++i) {
+                    const int c = c0 + i * blockDim.x;
+                    if (j0 + jj < k && c < c_end)
+                        v[i][jj] = __builtin_nontemporal_load(y + (int64_t)s_row[j0 + jj] * nvec + c);
+                }
 #pragma unroll
             for (int jj = 0; jj < kBatch; ++jj) {
                 if (j0 + jj >= k)
                     break;
                 const float wj = s_w[j0 + jj];
-                acc[0] = __builtin_fmaf(wj, bf16_lo(v[jj].x), acc[0]);
-                acc[1] = __builtin_fmaf(wj, bf16_hi(v[jj].x), acc[1]);
-                acc[2] = __builtin_fmaf(wj, bf16_lo(v[jj].y), acc[2]);
-                acc[3] = __builtin_fmaf(wj, bf16_hi(v[jj].y), acc[3]);
-                acc[4] = __builtin_fmaf(wj, bf16_lo(v[jj].z), acc[4]);
-                acc[5] = __builtin_fmaf(wj, bf16_hi(v[jj].z), acc[5]);
-                acc[6] = __builtin_fmaf(wj, bf16_lo(v[jj].w), acc[6]);
-                acc[7] = __builtin_fmaf(wj, bf16_hi(v[jj].w), acc[7]);
+#pragma unroll
+                for (int i = 0; i < kChunks; ++i) {
+                    acc[i][0] = __builtin_fmaf(wj, bf16_lo(v[i][jj].x), acc[i][0]);
+                    acc[i][1] = __builtin_fmaf(wj, bf16_hi(v[i][jj].x), acc[i][1]);
+                    acc[i][2] = __builtin_fmaf(wj, bf16_lo(v[i][jj].y), acc[i][2]);
+                    acc[i][3] = __builtin_fmaf(wj, bf16_hi(v[i][jj].y), acc[i][3]);
+                    acc[i][4] = __builtin_fmaf(wj, bf16_lo(v[i][jj].z), acc[i][4]);
+                    acc[i][5] = __builtin_fmaf(wj, bf16_hi(v[i][jj].z), acc[i][5]);
+                    acc[i][6] = __builtin_fmaf(wj, bf16_lo(v[i][jj].w), acc[i][6]);
+                    acc[i][7] = __builtin_fmaf(wj, bf16_hi(v[i][jj].w), acc[i][7]);
+                }
             }
         }
-        u32x4 o;
-        o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-        o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-        o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-        o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
-        __builtin_nontemporal_store(o, out + t * nvec + c);
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            const int c = c0 + i * blockDim.x;
+            if (c >= c_end)
+                continue;
+            u32x4 o;
+            o.x = f32_to_bf16(acc[i][0]) | (f32_to_bf16(acc[i][1]) << 16);
+            o.y = f32_to_bf16(acc[i][2]) | (f32_to_bf16(acc[i][3]) << 16);
+            o.z = f32_to_bf16(acc[i][4]) | (f32_to_bf16(acc[i][5]) << 16);
+            o.w = f32_to_bf16(acc[i][6]) | (f32_to_bf16(acc[i][7]) << 16);
+            __builtin_nontemporal_store(o, out + t * nvec + c);
+        }
     }
 }
 
@@ -87,8 +104,22 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 hipError_t launch_combine(const Geometry &g, const epx_layout &L, const void *y, const float *w,
                           int32_t hidden, void *out, hipStream_t stream)
 {
-    hipLaunchKernelGGL(combine_kernel, dim3(g.T), dim3(kThreads), 0, stream, (const u32x4 *)y,
-                       hidden / 8, (const int32_t *)L.slot, w, g.k, (u32x4 *)out,
+    const int nvec = hidden / 8;
+    // column slices so that small batches still give ~2048 workgroups
+    int want = g.T >= 2048 ? 1 : (2048 + g.T - 1) / g.T;
+    int slice = (nvec + want - 1) / want;
+    const int unit = kWave * kChunks;
+    slice = ((slice + unit - 1) / unit) * unit;
+    if (slice > nvec)
+        slice = nvec;
+    int threads = ((slice + kChunks - 1) / kChunks + kWave - 1) / kWave * kWave;
+    if (threads > 1024)
+        threads = 1024;
+    if (threads < kWave)
+        threads = kWave;
+    const dim3 grid(g.T, (nvec + slice - 1) / slice);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(threads), 0, stream, (const u32x4 *)y, nvec,
+                       slice, (const int32_t *)L.slot, w, g.k, (u32x4 *)out,
                        (const int32_t *)L.totals);
     return hipGetLastError();
 }

@@ -4,48 +4,64 @@
 // (DeepEP's default, Mode 1 of the digest "Balancing and Beyond:
 // Communication-Centric Optimizations in Expert Parallelism", section 3.2);
 // relay mode writes one copy per destination host (Mode 2 with
-// de-redundancy). Both read x once per token and store it to each of the
-// token's destination rows, so the kernel moves T*h*2 bytes in and
-// (rows)*h*2 bytes out: an HBM-bound scatter.
+// de-redundancy). Either way the kernel reads each token row once from HBM
+// and writes it to each of the token's destination rows: T*h*2 bytes in,
+// rows*h*2 bytes out, an HBM-bound scatter dominated by writes.
+//
+// Launch shape: one workgroup per (token, column slice); slices exist only to
+// give small batches enough workgroups. Each wave streams whole destination
+// rows (waves take the token's rows round-robin) in bursts of 4 KiB: every
+// lane loads 4 x 16 bytes of the token row (L2 serves the repeats) and
+// stores them with nontemporal 16-byte stores. Writing one row at a time per
+// wave keeps each wave's write stream contiguous, which this memory system
+// drains markedly faster than stores interleaved over all of a token's rows.
 //
 // The fp8 variant is the BF16-to-FP8 conversion that dispatch performs
 // (digest section 3.1): per token and 128-channel block, scale = amax/448 and
-// code = E4M3(x / scale), quantised once per token and stored to every row.
-// One 16-lane group holds a 128-channel block (8 bf16 per lane, one 16-byte
-// load), reduces the block maximum with lane shuffles and writes 8 code bytes
-// per lane (128 contiguous bytes per group).
+// code = E4M3(x / scale). The workgroup quantises its slice once into LDS (a
+// 16-lane group owns one 128-channel block: 8 bf16 per lane, block maximum by
+// lane shuffles), then the waves stream the codes and scales from LDS to the
+// destination rows.
 #include "epx_internal.h"
 
 namespace epx {
 namespace {
 
-constexpr int kThreads = 256;
-
-// Destination rows of token t: the layout's slots or relay slots.
-__device__ __forceinline__ void load_destinations(const int32_t *__restrict__ dest, int D,
-                                                  int64_t t, int32_t *s_dst)
-{
-    if (threadIdx.x < D)
-        s_dst[threadIdx.x] = dest[t * D + threadIdx.x];
-    __syncthreads();
-}
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kBurst = 4;              // 16-byte chunks per lane per burst
+constexpr int kMaxSliceVec = 4096;     // fp8 slice bound: LDS holds slice*8 code bytes
 
 __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
-    const u32x4 *__restrict__ x, int nvec, const int32_t *__restrict__ dest, int D,
+    const u32x4 *__restrict__ x, int nvec, int slice, const int32_t *__restrict__ dest, int D,
     u32x4 *__restrict__ recv, const int32_t *__restrict__ totals)
 {
-    __shared__ int32_t s_dst[kMaxTopk];
     if (totals[3] != 0)
         return;   // the layout saw out-of-range expert ids
     const int64_t t = blockIdx.x;
-    load_destinations(dest, D, t, s_dst);
+    const int c_beg = blockIdx.y * slice;
+    const int c_end = min(nvec, c_beg + slice);
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const u32x4 *xr = x + t * nvec;
-    for (int c = threadIdx.x; c < nvec; c += kThreads) {
-        const u32x4 v = __builtin_nontemporal_load(xr + c);
-        for (int d = 0; d < D; ++d) {
-            const int64_t r = s_dst[d];
-            if (r >= 0)
-                __builtin_nontemporal_store(v, recv + r * nvec + c);
+    for (int d = wave; d < D; d += kWaves) {
+        const int64_t r = dest[t * D + d];
+        if (r < 0)
+            continue;
+        u32x4 *dst = recv + r * nvec;
+        for (int c0 = c_beg + lane; c0 < c_end; c0 += kWave * kBurst) {
+            u32x4 v[kBurst];
+#pragma unroll
+            for (int i = 0; i < kBurst; ++i) {
+                const int c = c0 + i * kWave;
+                if (c < c_end)
+                    v[i] = xr[c];
+            }
+#pragma unroll
+            for (int i = 0; i < kBurst; ++i) {
+                const int c = c0 + i * kWave;
+                if (c < c_end)
+                    __builtin_nontemporal_store(v[i], dst + c);
+            }
         }
     }
 }
@@ -83,41 +99,72 @@ __device__ __forceinline__ uint32_t quantize4(float a, float b, float c, float d
            (f32_to_e4m3(d / s) << 24);
 }
 
+// Slice [c_beg, c_end) of token t, in 16-byte bf16 chunks (c_beg, c_end and
+// slice are multiples of 16 chunks = 128 channels). LDS: codes of the slice
+// (8 bytes per chunk) then one scale per 128-channel block.
 __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
-    const u32x4 *__restrict__ x, int nvec, const int32_t *__restrict__ dest, int D,
-    u32x2 *__restrict__ recv, float *__restrict__ scales, const int32_t *__restrict__ totals)
+    const u32x4 *__restrict__ x, int nvec, int slice, const int32_t *__restrict__ dest, int D,
+    uint8_t *__restrict__ recv, float *__restrict__ scales, const int32_t *__restrict__ totals)
 {
-    __shared__ int32_t s_dst[kMaxTopk];
+    extern __shared__ u32x4 s_codes[];   // slice/2 vectors of 16 codes
     if (totals[3] != 0)
         return;
     const int64_t t = blockIdx.x;
-    load_destinations(dest, D, t, s_dst);
-    const int nblk = nvec / 16;                     // 128-channel blocks per row
+    const int c_beg = blockIdx.y * slice;
+    const int c_end = min(nvec, c_beg + slice);
+    const int n = c_end - c_beg;                       // chunks in this slice
+    float *s_scale = (float *)(s_codes + (slice >> 1));
     const u32x4 *xr = x + t * nvec;
-    const int sub = threadIdx.x & 15;               // lane within the 16-lane group
-    for (int c = threadIdx.x; c < nvec; c += kThreads) {
-        const u32x4 v = __builtin_nontemporal_load(xr + c);
+
+    // quantise the slice once: 16 lanes per 128-channel block
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+        const u32x4 v = xr[c_beg + i];
         const float f0 = bf16_lo(v.x), f1 = bf16_hi(v.x), f2 = bf16_lo(v.y), f3 = bf16_hi(v.y);
         const float f4 = bf16_lo(v.z), f5 = bf16_hi(v.z), f6 = bf16_lo(v.w), f7 = bf16_hi(v.w);
         float m = fmaxf(fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))),
                         fmaxf(fmaxf(fabsf(f4), fabsf(f5)), fmaxf(fabsf(f6), fabsf(f7))));
 #pragma unroll
-        for (int d = 8; d > 0; d >>= 1)
-            m = fmaxf(m, __shfl_xor(m, d, 16));
+        for (int dd = 8; dd > 0; dd >>= 1)
+            m = fmaxf(m, __shfl_xor(m, dd, 16));
         const float s = m / 448.0f;
         const bool zero = (m == 0.0f);
         u32x2 q;
         q.x = quantize4(f0, f1, f2, f3, s, zero);
         q.y = quantize4(f4, f5, f6, f7, s, zero);
-        const int blk = c >> 4;
-        for (int d = 0; d < D; ++d) {
-            const int64_t r = s_dst[d];
-            if (r < 0)
-                continue;
-            __builtin_nontemporal_store(q, recv + r * nvec + c);
-            if (sub == 0)
-                scales[r * nblk + blk] = s;
+        ((u32x2 *)s_codes)[i] = q;
+        if ((i & 15) == 0)
+            s_scale[i >> 4] = s;
+    }
+    __syncthreads();
+
+    // stream codes (16 bytes = 16 codes per lane) and scales to each row
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int nq = n >> 1;                 // 16-byte code vectors in the slice
+    const int nblk = n >> 4;               // scales in the slice
+    const int row_vec = nvec >> 1;         // 16-byte code vectors per row
+    const int row_blk = nvec >> 4;         // scales per row
+    for (int d = wave; d < D; d += kWaves) {
+        const int64_t r = dest[t * D + d];
+        if (r < 0)
+            continue;
+        u32x4 *dst = (u32x4 *)(recv) + r * row_vec + (c_beg >> 1);
+        for (int c0 = lane; c0 < nq; c0 += kWave * kBurst) {
+            u32x4 v[kBurst];
+#pragma unroll
+            for (int i = 0; i < kBurst; ++i) {
+                const int c = c0 + i * kWave;
+                if (c < nq)
+                    v[i] = s_codes[c];
+            }
+#pragma unroll
+            for (int i = 0; i < kBurst; ++i) {
+                const int c = c0 + i * kWave;
+                if (c < nq)
+                    __builtin_nontemporal_store(v[i], dst + c);
+            }
         }
+        for (int b = lane; b < nblk; b += kWave)
+            scales[r * row_blk + (c_beg >> 4) + b] = s_scale[b];
     }
 }
 
@@ -129,6 +176,20 @@ __global__ void f32_to_e4m3_kernel(const float *__restrict__ in, uint8_t *__rest
         out[i] = (uint8_t)f32_to_e4m3(in[i]);
 }
 
+// Column slices per token: enough workgroups to cover the GPU (about 2048)
+// when the batch is small; each slice a whole number of `align` chunks.
+int slice_width(int T, int nvec, int align, int max_width)
+{
+    int want = T >= 2048 ? 1 : (2048 + T - 1) / T;
+    int width = (nvec + want - 1) / want;
+    width = ((width + align - 1) / align) * align;
+    if (width < 4 * align && nvec > 4 * align)
+        width = 4 * align;        // no slice below 4 alignment units
+    if (width > max_width)
+        width = (max_width / align) * align;
+    return width < nvec ? width : nvec;
+}
+
 }  // namespace
 
 hipError_t launch_dispatch_bf16(const Geometry &g, const epx_layout &L, const void *x,
@@ -136,9 +197,11 @@ hipError_t launch_dispatch_bf16(const Geometry &g, const epx_layout &L, const vo
 {
     const int32_t *dest = g.relay ? L.relay_slot : L.slot;
     const int D = g.relay ? g.H : g.k;
-    hipLaunchKernelGGL(dispatch_bf16_kernel, dim3(g.T), dim3(kThreads), 0, stream,
-                       (const u32x4 *)x, hidden / 8, dest, D, (u32x4 *)recv,
-                       (const int32_t *)L.totals);
+    const int nvec = hidden / 8;
+    const int slice = slice_width(g.T, nvec, kWave, 1 << 30);
+    const dim3 grid(g.T, (nvec + slice - 1) / slice);
+    hipLaunchKernelGGL(dispatch_bf16_kernel, grid, dim3(kThreads), 0, stream, (const u32x4 *)x,
+                       nvec, slice, dest, D, (u32x4 *)recv, (const int32_t *)L.totals);
     return hipGetLastError();
 }
 
@@ -147,9 +210,12 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const epx_layout &L, const voi
 {
     const int32_t *dest = g.relay ? L.relay_slot : L.slot;
     const int D = g.relay ? g.H : g.k;
-    hipLaunchKernelGGL(dispatch_fp8_kernel, dim3(g.T), dim3(kThreads), 0, stream,
-                       (const u32x4 *)x, hidden / 8, dest, D, (u32x2 *)recv, scales,
-                       (const int32_t *)L.totals);
+    const int nvec = hidden / 8;          // multiple of 16 (hidden % 128 == 0)
+    const int slice = slice_width(g.T, nvec, 16, kMaxSliceVec);
+    const dim3 grid(g.T, (nvec + slice - 1) / slice);
+    const size_t lds = (size_t)slice * 8 + (size_t)(slice / 16) * sizeof(float);
+    hipLaunchKernelGGL(dispatch_fp8_kernel, grid, dim3(kThreads), lds, stream, (const u32x4 *)x,
+                       nvec, slice, dest, D, (uint8_t *)recv, scales, (const int32_t *)L.totals);
     return hipGetLastError();
 }
 

@@ -10,21 +10,41 @@
 namespace epx {
 
 constexpr int kWave = 64;            // CDNA wavefront width
-constexpr int kChunkTokens = 64;     // tokens per layout workgroup (one per lane in the relay pass)
+constexpr int kChunkPairs = 1024;    // pairs staged per layout workgroup (at most 64 tokens)
 constexpr int kMaxExperts = 2048;
 constexpr int kMaxTopk = 64;
 constexpr int kMaxHosts = 64;
 constexpr int kMaxRanksPerHost = 32;
 constexpr int kFp8Block = 128;       // channels per fp8 scale
 
+// Division by a divisor fixed per call, as a multiply-high: q = umulhi(n, m)
+// with m = ceil(2^32 / d) is exact whenever n * d < 2^32 (the error n*(m -
+// 2^32/d)/2^32 stays below 1/d). Every use here has n, d <= 4096.
+struct FastDiv {
+    uint32_t mul;   // ceil(2^32 / d); unused when d == 1
+    int32_t d;
+    void init(int32_t divisor)
+    {
+        d = divisor;
+        mul = divisor == 1 ? 0u : (uint32_t)((((uint64_t)1 << 32) + divisor - 1) / divisor);
+    }
+    __device__ __forceinline__ int32_t div(int32_t n) const
+    {
+        return d == 1 ? n : (int32_t)__umulhi((uint32_t)n, mul);
+    }
+};
+
 // Problem geometry, validated on the host and passed by value to kernels.
 struct Geometry {
     int32_t T, k, E, R, H, s;
     int32_t epr;     // experts per rank
     int32_t rph;     // ranks per host
-    int32_t G;       // layout workgroups = max(1, ceil(T / kChunkTokens))
+    int32_t ct;      // tokens per layout workgroup: min(64, kChunkPairs / k)
+    int32_t G;       // layout workgroups = max(1, ceil(T / ct))
+    int32_t Gs;      // workspace column stride: G rounded up to 4 (16-byte columns)
     int32_t nbits;   // bits that distinguish expert ids (ceil(log2 E))
     int32_t relay;   // HOST_RELAY mode
+    FastDiv div_epr, div_rph, div_k;
 };
 
 // 16-byte and 8-byte native vectors (global_load/store_dwordx4, dwordx2).

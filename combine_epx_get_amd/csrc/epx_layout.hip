@@ -9,20 +9,20 @@
 // per-rank token counts are those of the DeepEP issue "[GH-ISSUE #250]
 // Profiling when rank unbalance".
 //
-// Three launches, no atomics on global memory and no zero-filled buffers:
-//   count  (G workgroups, 64 tokens each): LDS-privatised histograms of
-//          experts, of distinct ranks and hosts per token, and of bad ids;
-//          each workgroup writes one column entry ws[col * G + b].
-//   scan   (one wave per column): exclusive scan of every column over the G
-//          workgroups with a wave-wide shuffle scan; the column total is the
-//          global count.
-//   assign (G workgroups): prefix of the expert counts in LDS; wave 0 walks
-//          the workgroup's pairs in (token, j) order, 64 at a time, groups
-//          equal expert ids with ceil(log2 E) ballots (a wave-level
-//          multisplit) and takes rank-in-group = popcount(peers below me),
-//          so positions are stable and independent of atomic order; wave 1
-//          assigns relay rows, one token per lane, host by host with one
-//          ballot each.
+// Row order: per-expert rows by (expert, token, j); relay rows by (host,
+// token). Positions come from ordered wave walks, never from atomic order:
+// a wave takes 64 pairs at a time in (t, j) order, groups equal expert ids
+// with ceil(log2 E) ballots (a wave-level multisplit) and gives each lane
+// base + popcount(peers below it); the group's first lane then advances the
+// base. Counting may use LDS atomics, because counts do not depend on order.
+//
+// Three shapes, no global atomics and no zero-filled buffers:
+//   small batches (<= 4096 pairs): one workgroup does everything in LDS;
+//   up to 64 workgroups of up to 64 tokens: count, then assign (each assign
+//     workgroup sums the count columns itself);
+//   more: count, a column scan (one wave per counter), assign.
+// Every per-pair rank and host is computed once, with division constants
+// prepared on the host, and staged in LDS with the chunk's ids.
 #include "epx_internal.h"
 
 namespace epx {
@@ -50,10 +50,117 @@ __device__ __forceinline__ int wave_max(int v)
     return v;
 }
 
+// Lanes whose `e` equals mine among the active lanes (ballot multisplit).
+__device__ __forceinline__ uint64_t match_peers(bool active, int e, int nbits)
+{
+    uint64_t peers = __ballot(active);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const bool on = (e >> bit) & 1;
+        const uint64_t m = __ballot(on);
+        peers &= on ? m : ~m;
+    }
+    return peers;
+}
+
+// Stage pairs [0, np) of a chunk: ids, their ranks and hosts (-1 for a bad id).
+__device__ __forceinline__ void stage_pairs(const int32_t *__restrict__ idx, int64_t p0, int np,
+                                            const Geometry &g, int32_t *s_idx, int32_t *s_rk,
+                                            int32_t *s_hk, int nthreads)
+{
+    for (int p = threadIdx.x; p < np; p += nthreads) {
+        const int e = idx[p0 + p];
+        const bool ok = (unsigned)e < (unsigned)g.E;
+        const int r = ok ? g.div_epr.div(e) : -1;
+        s_idx[p] = e;
+        s_rk[p] = r;
+        s_hk[p] = ok ? g.div_rph.div(r) : -1;
+    }
+}
+
+// For pair p of a staged chunk (token-major, k per token): count the expert,
+// and the pair's rank / host when no earlier pair of the same token has it.
+__device__ __forceinline__ void count_pair(int p, const Geometry &g, const int32_t *s_idx,
+                                           const int32_t *s_rk, const int32_t *s_hk,
+                                           int32_t *s_hist, int32_t *s_rtok, int32_t *s_htok,
+                                           int32_t *s_bad)
+{
+    const int r = s_rk[p];
+    if (r < 0) {
+        atomicAdd(s_bad, 1);
+        return;
+    }
+    atomicAdd(&s_hist[s_idx[p]], 1);
+    const int first = g.div_k.div(p) * g.k;   // first pair of the token
+    const int h = s_hk[p];
+    bool new_rank = true, new_host = true;
+    for (int q = first; q < p; ++q) {
+        new_rank = new_rank && s_rk[q] != r;
+        new_host = new_host && s_hk[q] != h;
+    }
+    if (new_rank)
+        atomicAdd(&s_rtok[r], 1);
+    if (new_host)
+        atomicAdd(&s_htok[h], 1);
+}
+
+// Relay rows of one token on one lane of a wave holding up to 64 consecutive
+// tokens: for each host, rows of the tokens that touch it, in token order,
+// from `base(h)` on. Every lane of the wave must call it (ballots).
+template <typename Base>
+__device__ __forceinline__ void relay_rows(bool act, int t, const int32_t *ids, const int32_t *rks,
+                                           const int32_t *hks, const Geometry &g, Base base,
+                                           const epx_layout &L)
+{
+    const uint64_t below = (1ull << lane_id()) - 1ull;
+    uint64_t hosts = 0;
+    if (act)
+        for (int j = 0; j < g.k; ++j)
+            hosts |= 1ull << hks[j];
+    for (int h = 0; h < g.H; ++h) {
+        const bool has = (hosts >> h) & 1ull;
+        const uint64_t bal = __ballot(has);
+        if (!act)
+            continue;
+        if (!has) {
+            L.relay_slot[(int64_t)t * g.H + h] = -1;
+            continue;
+        }
+        const int r = base(h) + __popcll(bal & below);
+        L.relay_slot[(int64_t)t * g.H + h] = r;
+        L.relay_token[r] = t;
+        uint32_t mask = 0;
+        for (int j = 0; j < g.k; ++j) {
+            const bool here = hks[j] == h;
+            L.fanout_expert[(int64_t)r * g.k + j] = here ? ids[j] : -1;
+            if (here)
+                mask |= 1u << (rks[j] - h * g.rph);
+        }
+        L.fanout_rank_mask[r] = mask;
+    }
+}
+
+// Relay rows past the used ones, [used, capacity) split over `parts`, read as empty.
+__device__ __forceinline__ void clear_relay_tail(const Geometry &g, int64_t used, int part,
+                                                 int parts, int nthreads, const epx_layout &L)
+{
+    const int64_t cap = (int64_t)g.T * min(g.k, g.H);
+    const int64_t per = (cap + parts - 1) / parts;
+    const int64_t beg = max(used, (int64_t)part * per), end = min(cap, (int64_t)(part + 1) * per);
+    for (int64_t r = beg + threadIdx.x; r < end; r += nthreads) {
+        L.relay_token[r] = -1;
+        L.fanout_rank_mask[r] = 0u;
+    }
+    for (int64_t i = beg * g.k + threadIdx.x; i < end * g.k; i += nthreads)
+        L.fanout_expert[i] = -1;
+}
+
 // ---------------------------------------------------------------- count
-// LDS columns: [0, E) experts, [E, E+R) ranks, [E+R, E+R+H) hosts, E+R+H bad ids.
-__global__ __launch_bounds__(256) void layout_count_kernel(const int32_t *__restrict__ idx,
-                                                           Geometry g, int32_t *__restrict__ ws)
+// Columns of the per-workgroup counts: [0, E) experts, [E, E+R) ranks,
+// [E+R, E+R+H) hosts, E+R+H bad ids; column c of workgroup b at ws[c*Gs + b].
+constexpr int kCountThreads = 256;
+
+__global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
+    const int32_t *__restrict__ idx, Geometry g, int32_t *__restrict__ ws)
 {
     extern __shared__ int32_t lds[];
     const int ncol = g.E + g.R + g.H + 1;
@@ -61,66 +168,36 @@ __global__ __launch_bounds__(256) void layout_count_kernel(const int32_t *__rest
     int32_t *s_rtok = lds + g.E;
     int32_t *s_htok = s_rtok + g.R;
     int32_t *s_bad = s_htok + g.H;
+    int32_t *s_idx = lds + ncol;
+    int32_t *s_rk = s_idx + g.ct * g.k;
+    int32_t *s_hk = s_rk + g.ct * g.k;
 
     const int b = blockIdx.x;
-    const int t0 = b * kChunkTokens;
-    const int nt = max(0, min(kChunkTokens, g.T - t0));
-    for (int i = threadIdx.x; i < ncol; i += blockDim.x)
-        lds[i] = 0;
-    __syncthreads();
-
-    const int64_t p0 = (int64_t)t0 * g.k;
+    const int t0 = b * g.ct;
+    const int nt = max(0, min(g.ct, g.T - t0));
     const int np = nt * g.k;
-    for (int p = threadIdx.x; p < np; p += blockDim.x) {
-        const int e = idx[p0 + p];
-        if ((unsigned)e < (unsigned)g.E)
-            atomicAdd(&s_hist[e], 1);
-        else
-            atomicAdd(s_bad, 1);
-    }
-    if (threadIdx.x < nt) {
-        const int32_t *row = idx + p0 + (int64_t)threadIdx.x * g.k;
-        uint64_t hosts = 0;
-        for (int j = 0; j < g.k; ++j) {
-            const int e = row[j];
-            if ((unsigned)e >= (unsigned)g.E)
-                continue;
-            const int r = e / g.epr;
-            bool first = true;
-            for (int i = 0; i < j; ++i) {
-                const int e2 = row[i];
-                if ((unsigned)e2 < (unsigned)g.E && e2 / g.epr == r) {
-                    first = false;
-                    break;
-                }
-            }
-            if (first)
-                atomicAdd(&s_rtok[r], 1);
-            const int h = r / g.rph;
-            if (!((hosts >> h) & 1ull)) {
-                hosts |= 1ull << h;
-                atomicAdd(&s_htok[h], 1);
-            }
-        }
-    }
+    for (int i = threadIdx.x; i < ncol; i += kCountThreads)
+        lds[i] = 0;
+    stage_pairs(idx, (int64_t)t0 * g.k, np, g, s_idx, s_rk, s_hk, kCountThreads);
     __syncthreads();
-    for (int c = threadIdx.x; c < ncol; c += blockDim.x)
-        ws[(int64_t)c * g.G + b] = lds[c];
+    for (int p = threadIdx.x; p < np; p += kCountThreads)
+        count_pair(p, g, s_idx, s_rk, s_hk, s_hist, s_rtok, s_htok, s_bad);
+    __syncthreads();
+    for (int c = threadIdx.x; c < ncol; c += kCountThreads)
+        ws[(int64_t)c * g.Gs + b] = lds[c];
 }
 
 // ---------------------------------------------------------------- scan
-__global__ __launch_bounds__(256) void layout_scan_kernel(Geometry g, int32_t *__restrict__ ws,
-                                                          int32_t *__restrict__ expert_count,
-                                                          int32_t *__restrict__ rank_tokens,
-                                                          int32_t *__restrict__ host_tokens,
-                                                          int32_t *__restrict__ totals)
+// One wave per column: exclusive scan over the G workgroups in place; the
+// column total goes to ws_tot[c] (ws_tot = ws + ncol*Gs).
+__global__ __launch_bounds__(256) void layout_scan_kernel(Geometry g, int32_t *__restrict__ ws)
 {
     const int ncol = g.E + g.R + g.H + 1;
     const int col = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (col >= ncol)
         return;
     const int lane = lane_id();
-    int32_t *c = ws + (int64_t)col * g.G;
+    int32_t *c = ws + (int64_t)col * g.Gs;
     int carry = 0;
     for (int base = 0; base < g.G; base += kWave) {
         const int i = base + lane;
@@ -130,24 +207,15 @@ __global__ __launch_bounds__(256) void layout_scan_kernel(Geometry g, int32_t *_
             c[i] = carry + incl - v;
         carry += __shfl(incl, kWave - 1, kWave);
     }
-    if (lane == 0) {
-        if (col < g.E)
-            expert_count[col] = carry;
-        else if (col < g.E + g.R)
-            rank_tokens[col - g.E] = carry;
-        else if (col < g.E + g.R + g.H)
-            host_tokens[col - g.E - g.R] = carry;
-        else
-            totals[3] = carry;
-    }
+    if (lane == 0)
+        ws[(int64_t)ncol * g.Gs + col] = carry;
 }
 
 // ---------------------------------------------------------------- assign
 constexpr int kAssignThreads = 128;
 
-// Exclusive scan of src[0, n) (global) into dst[0, n] (LDS), dst[n] = total.
-__device__ void block_exclusive_scan(const int32_t *__restrict__ src, int32_t *dst, int n,
-                                     int32_t *s_wsum)
+// Exclusive scan of src[0, n) (LDS) into dst[0, n] (LDS), dst[n] = total.
+__device__ void block_exclusive_scan(const int32_t *src, int32_t *dst, int n, int32_t *s_wsum)
 {
     const int tid = threadIdx.x;
     const int per = (n + kAssignThreads - 1) / kAssignThreads;
@@ -161,30 +229,72 @@ __device__ void block_exclusive_scan(const int32_t *__restrict__ src, int32_t *d
     __syncthreads();
     int run = incl - sum + (tid >= kWave ? s_wsum[0] : 0);
     for (int i = beg; i < end; ++i) {
+        const int v = src[i];
         dst[i] = run;
-        run += src[i];
+        run += v;
     }
     if (tid == kAssignThreads - 1)
         dst[n] = run;
 }
 
+// SUMS: this workgroup sums the raw count columns itself (total and the
+// prefix over workgroups before it); otherwise the scan kernel has left the
+// prefix in place and the totals after the columns.
+template <bool SUMS>
 __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
     const int32_t *__restrict__ idx, Geometry g, const int32_t *__restrict__ ws, epx_layout L)
 {
     extern __shared__ int32_t lds[];
-    int32_t *s_eoff = lds;                 // [E + 1]
-    int32_t *s_base = s_eoff + g.E + 1;    // [E]  running row per expert
-    int32_t *s_hoff = s_base + g.E;        // [H + 1]
+    const int ncol = g.E + g.R + g.H + 1;
+    const int kc = g.ct * g.k;
+    int32_t *s_tot = lds;                  // [ncol] column totals
+    int32_t *s_pre = s_tot + ncol;         // [ncol] this workgroup's prefix per column
+    int32_t *s_eoff = s_pre + ncol;        // [E + 1]
+    int32_t *s_hoff = s_eoff + g.E + 1;    // [H + 1]
+    int32_t *s_idx = s_hoff + g.H + 1;     // [64 k] ids, ranks, hosts of the chunk
+    int32_t *s_rk = s_idx + kc;
+    int32_t *s_hk = s_rk + kc;
     __shared__ int32_t s_wsum[2];
     __shared__ int32_t s_wmax[2];
-    __shared__ int32_t s_bad;
 
     const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-    if (tid == 0)
-        s_bad = L.totals[3];
-    block_exclusive_scan(L.expert_count, s_eoff, g.E, s_wsum);
+    const int t0 = b * g.ct;
+    const int nt = max(0, min(g.ct, g.T - t0));
+    const int64_t p0 = (int64_t)t0 * g.k;
+
+    stage_pairs(idx, p0, nt * g.k, g, s_idx, s_rk, s_hk, kAssignThreads);
+    if (SUMS) {
+        // each thread sums whole columns as 16-byte vectors (Gs % 4 == 0)
+        for (int c = tid; c < ncol; c += kAssignThreads) {
+            const int4 *col = (const int4 *)(ws + (int64_t)c * g.Gs);
+            int tot = 0, pre = 0;
+            for (int i = 0; i < g.Gs / 4; ++i) {
+                const int4 v = col[i];
+                const int i0 = 4 * i;   // entries [G, Gs) are padding, never written
+                tot += (i0 < g.G ? v.x : 0) + (i0 + 1 < g.G ? v.y : 0) +
+                       (i0 + 2 < g.G ? v.z : 0) + (i0 + 3 < g.G ? v.w : 0);
+                pre += (i0 < b ? v.x : 0) + (i0 + 1 < b ? v.y : 0) + (i0 + 2 < b ? v.z : 0) +
+                       (i0 + 3 < b ? v.w : 0);
+            }
+            s_tot[c] = tot;
+            s_pre[c] = pre;
+        }
+    } else {
+        for (int c = tid; c < ncol; c += kAssignThreads) {
+            s_tot[c] = ws[(int64_t)ncol * g.Gs + c];
+            s_pre[c] = ws[(int64_t)c * g.Gs + b];
+        }
+    }
+    __syncthreads();
+    const int bad = s_tot[ncol - 1];
+    if (bad != 0) {
+        if (b == 0 && tid == 0)
+            L.totals[3] = bad;
+        return;   // out-of-range ids: nothing else is defined
+    }
+    block_exclusive_scan(s_tot, s_eoff, g.E, s_wsum);
     if (wave == 0) {
-        const int v = lane < g.H ? L.host_tokens[lane] : 0;
+        const int v = lane < g.H ? s_tot[g.E + g.R + lane] : 0;
         const int incl = wave_inclusive_scan(v);
         if (lane < g.H)
             s_hoff[lane] = incl - v;
@@ -192,25 +302,30 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
             s_hoff[g.H] = incl;
     }
     __syncthreads();
-    if (s_bad != 0)
-        return;   // out-of-range ids: nothing below is defined
 
     if (b == 0) {
-        for (int e = tid; e <= g.E; e += kAssignThreads)
+        for (int e = tid; e <= g.E; e += kAssignThreads) {
             L.expert_offset[e] = s_eoff[e];
+            if (e < g.E)
+                L.expert_count[e] = s_tot[e];
+        }
         for (int r = tid; r <= g.R; r += kAssignThreads) {
             L.rank_offset[r] = s_eoff[r * g.epr];
-            if (r < g.R)
+            if (r < g.R) {
                 L.rank_rows[r] = s_eoff[(r + 1) * g.epr] - s_eoff[r * g.epr];
+                L.rank_tokens[r] = s_tot[g.E + r];
+            }
         }
         for (int h = tid; h <= g.H; h += kAssignThreads) {
             L.host_offset[h] = s_hoff[h];
-            if (h < g.H)
+            if (h < g.H) {
+                L.host_tokens[h] = s_tot[g.E + g.R + h];
                 L.relay_dst_rank[h] = h * g.rph + g.s % g.rph;
+            }
         }
         int m = 0;
         for (int e = tid; e < g.E; e += kAssignThreads)
-            m = max(m, s_eoff[e + 1] - s_eoff[e]);
+            m = max(m, s_tot[e]);
         m = wave_max(m);
         if (lane == 0)
             s_wmax[wave] = m;
@@ -219,87 +334,251 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
             L.totals[0] = g.T * g.k;
             L.totals[1] = s_hoff[g.H];
             L.totals[2] = max(s_wmax[0], s_wmax[1]);
+            L.totals[3] = 0;
         }
     }
 
-    for (int e = tid; e < g.E; e += kAssignThreads)
-        s_base[e] = s_eoff[e] + ws[(int64_t)e * g.G + b];
-    __syncthreads();
-
-    const int t0 = b * kChunkTokens;
-    const int nt = max(0, min(kChunkTokens, g.T - t0));
-    const int64_t p0 = (int64_t)t0 * g.k;
-    const uint64_t below = (1ull << lane) - 1ull;
-
     if (wave == 0) {
-        // Stable rows: pairs in (token, j) order, 64 per step.
+        // rows per expert in (t, j) order: base = offset + rows of earlier workgroups
+        for (int e = lane; e < g.E; e += kWave)
+            s_eoff[e] += s_pre[e];
+        const uint64_t below = (1ull << lane) - 1ull;
         const int np = nt * g.k;
         for (int base = 0; base < np; base += kWave) {
             const int p = base + lane;
             const bool act = p < np;
-            const int e = act ? idx[p0 + p] : 0;
-            uint64_t peers = __ballot(act);
-            for (int bit = 0; bit < g.nbits; ++bit) {
-                const bool on = (e >> bit) & 1;
-                const uint64_t m = __ballot(on);
-                peers &= on ? m : ~m;
-            }
+            const int e = act ? s_idx[p] : 0;
+            const uint64_t peers = match_peers(act, e, g.nbits);
             if (act) {
                 const int before = __popcll(peers & below);
-                const int first = s_base[e];
+                const int first = s_eoff[e];
                 const int row = first + before;
                 L.slot[p0 + p] = row;
-                L.row_token[row] = t0 + p / g.k;
+                L.row_token[row] = t0 + g.div_k.div(p);
                 if (before == 0)
-                    s_base[e] = first + __popcll(peers);
+                    s_eoff[e] = first + __popcll(peers);
             }
         }
     } else if (g.relay) {
-        // Relay rows: host by host, tokens of this chunk in order (one per lane).
-        const bool act = lane < nt;
-        const int t = t0 + lane;
-        const int32_t *row = idx + (int64_t)t * g.k;
-        uint64_t hosts = 0;
-        if (act)
-            for (int j = 0; j < g.k; ++j)
-                hosts |= 1ull << (row[j] / g.epr / g.rph);
-        for (int h = 0; h < g.H; ++h) {
-            const bool has = (hosts >> h) & 1ull;
-            const uint64_t bal = __ballot(has);
-            if (!act)
-                continue;
-            if (!has) {
-                L.relay_slot[(int64_t)t * g.H + h] = -1;
-                continue;
-            }
-            const int r = s_hoff[h] + ws[(int64_t)(g.E + g.R + h) * g.G + b] + __popcll(bal & below);
-            L.relay_slot[(int64_t)t * g.H + h] = r;
-            L.relay_token[r] = t;
-            uint32_t mask = 0;
-            for (int j = 0; j < g.k; ++j) {
-                const int e = row[j];
-                const bool here = e / g.epr / g.rph == h;
-                L.fanout_expert[(int64_t)r * g.k + j] = here ? e : -1;
-                if (here)
-                    mask |= 1u << ((e / g.epr) % g.rph);
-            }
-            L.fanout_rank_mask[r] = mask;
+        const int o = lane * g.k;
+        relay_rows(lane < nt, t0 + lane, s_idx + o, s_rk + o, s_hk + o, g,
+                   [&](int h) { return s_hoff[h] + s_pre[g.E + g.R + h]; }, L);
+    }
+    if (g.relay)
+        clear_relay_tail(g, s_hoff[g.H], b, g.G, kAssignThreads, L);
+}
+
+// ---------------------------------------------------------------- single workgroup
+// Small batches (decode): the whole layout in one workgroup of 16 waves, in
+// LDS, in one launch. Wave w owns a contiguous range of pairs (in (t, j)
+// order) and, in relay mode, tokens [64w, 64w + 64). Per-wave counts per
+// expert (and per host) are scanned over the waves, which gives every wave
+// the base of its first row for each expert; the ordered walk then assigns
+// rows exactly as the multi-workgroup path does.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / kWave;
+
+__global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
+    const int32_t *__restrict__ idx, Geometry g, epx_layout L)
+{
+    extern __shared__ int32_t lds[];
+    const int P = g.T * g.k;
+    int32_t *s_idx = lds;                              // [P] ids, ranks, hosts
+    int32_t *s_rk = s_idx + P;
+    int32_t *s_hk = s_rk + P;
+    int32_t *s_cnt = s_hk + P;                         // [waves][E] counts, then row bases
+    int32_t *s_eoff = s_cnt + kSmallWaves * g.E;       // [E + 1]
+    int32_t *s_rtok = s_eoff + g.E + 1;                // [R]
+    int32_t *s_htok = s_rtok + g.R;                    // [H]
+    int32_t *s_hcnt = s_htok + g.H;                    // [waves][H] counts, then relay bases
+    int32_t *s_hoff = s_hcnt + kSmallWaves * g.H;      // [H + 1]
+    __shared__ int32_t s_bad;
+    __shared__ int32_t s_wsum[kSmallWaves];
+    __shared__ int32_t s_wmax[kSmallWaves];
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const uint64_t below = (1ull << lane) - 1ull;
+
+    stage_pairs(idx, 0, P, g, s_idx, s_rk, s_hk, kSmallThreads);
+    for (int i = tid; i < kSmallWaves * g.E; i += kSmallThreads)
+        s_cnt[i] = 0;
+    for (int i = tid; i < g.R; i += kSmallThreads)
+        s_rtok[i] = 0;
+    for (int i = tid; i < g.H; i += kSmallThreads)
+        s_htok[i] = 0;
+    if (tid == 0)
+        s_bad = 0;
+    __syncthreads();
+
+    // per-wave counts per expert (the first lane of each group adds its size)
+    const int per_wave = (P + kSmallThreads - 1) / kSmallThreads * kWave;
+    const int pw0 = wave * per_wave, pw1 = min(P, pw0 + per_wave);
+    for (int base = pw0; base < pw1; base += kWave) {
+        const int p = base + lane;
+        const bool act = p < pw1;
+        const int e = act ? s_idx[p] : 0;
+        const bool ok = act && s_rk[p] >= 0;
+        const uint64_t peers = match_peers(ok, e, g.nbits);
+        if (ok && (peers & below) == 0ull)
+            s_cnt[wave * g.E + e] += __popcll(peers);
+    }
+    // bad ids, distinct ranks and hosts per token
+    for (int p = tid; p < P; p += kSmallThreads) {
+        const int r = s_rk[p];
+        if (r < 0) {
+            atomicAdd(&s_bad, 1);
+            continue;
         }
+        const int first = g.div_k.div(p) * g.k;
+        const int h = s_hk[p];
+        bool new_rank = true, new_host = true;
+        for (int q = first; q < p; ++q) {
+            new_rank = new_rank && s_rk[q] != r;
+            new_host = new_host && s_hk[q] != h;
+        }
+        if (new_rank)
+            atomicAdd(&s_rtok[r], 1);
+        if (new_host)
+            atomicAdd(&s_htok[h], 1);
+    }
+    // per-wave relay counts: tokens of wave w touching host h
+    uint64_t hosts = 0;
+    if (tid < g.T)
+        for (int j = 0; j < g.k; ++j) {
+            const int h = s_hk[tid * g.k + j];
+            if (h >= 0)
+                hosts |= 1ull << h;
+        }
+    for (int h = 0; h < g.H; ++h) {
+        const uint64_t bal = __ballot((hosts >> h) & 1ull);
+        if (lane == 0)
+            s_hcnt[wave * g.H + h] = __popcll(bal);
+    }
+    __syncthreads();
+    if (s_bad != 0) {
+        if (tid == 0)
+            L.totals[3] = s_bad;
+        return;   // out-of-range ids: nothing else is defined
     }
 
-    if (g.relay) {
-        // Unused relay rows [relay_rows, capacity) read as empty.
-        const int64_t cap = (int64_t)g.T * min(g.k, g.H);
-        const int64_t used = s_hoff[g.H];
-        const int64_t per = (cap + g.G - 1) / g.G;
-        const int64_t beg = max(used, (int64_t)b * per), end = min(cap, (int64_t)(b + 1) * per);
-        for (int64_t r = beg + tid; r < end; r += kAssignThreads) {
-            L.relay_token[r] = -1;
-            L.fanout_rank_mask[r] = 0u;
+    // scans over waves: each wave's base per expert / per host, and totals
+    if (tid < g.E) {
+        int run = 0;
+        for (int w = 0; w < kSmallWaves; ++w) {
+            const int c = s_cnt[w * g.E + tid];
+            s_cnt[w * g.E + tid] = run;
+            run += c;
         }
-        for (int64_t i = beg * g.k + tid; i < end * g.k; i += kAssignThreads)
-            L.fanout_expert[i] = -1;
+        s_eoff[tid] = run;
+    } else if (tid >= kSmallThreads - kWave && tid - (kSmallThreads - kWave) < g.H) {
+        const int h = tid - (kSmallThreads - kWave);
+        int run = 0;
+        for (int w = 0; w < kSmallWaves; ++w) {
+            const int c = s_hcnt[w * g.H + h];
+            s_hcnt[w * g.H + h] = run;
+            run += c;
+        }
     }
+    __syncthreads();
+    const int cnt_e = tid < g.E ? s_eoff[tid] : 0;
+    const int incl = wave_inclusive_scan(cnt_e);
+    if (lane == kWave - 1)
+        s_wsum[wave] = incl;
+    const int m = wave_max(cnt_e);
+    if (lane == 0)
+        s_wmax[wave] = m;
+    __syncthreads();
+    if (wave == 0) {
+        const int v = lane < kSmallWaves ? s_wsum[lane] : 0;
+        const int vi = wave_inclusive_scan(v);
+        const int mm = wave_max(lane < kSmallWaves ? s_wmax[lane] : 0);
+        if (lane < kSmallWaves)
+            s_wsum[lane] = vi - v;
+        if (lane == 0)
+            s_wmax[0] = mm;
+    } else if (wave == 1) {
+        const int v = lane < g.H ? s_htok[lane] : 0;
+        const int vi = wave_inclusive_scan(v);
+        if (lane < g.H)
+            s_hoff[lane] = vi - v;
+        if (lane == kWave - 1)
+            s_hoff[g.H] = vi;
+    }
+    __syncthreads();
+    if (tid < g.E) {
+        const int ex = incl - cnt_e + s_wsum[wave];
+        s_eoff[tid] = ex;
+        if (tid == g.E - 1)
+            s_eoff[g.E] = ex + cnt_e;
+    }
+    __syncthreads();
+
+    // global counts and offsets
+    for (int e = tid; e <= g.E; e += kSmallThreads) {
+        L.expert_offset[e] = s_eoff[e];
+        if (e < g.E)
+            L.expert_count[e] = s_eoff[e + 1] - s_eoff[e];
+    }
+    for (int r = tid; r <= g.R; r += kSmallThreads) {
+        L.rank_offset[r] = s_eoff[r * g.epr];
+        if (r < g.R) {
+            L.rank_rows[r] = s_eoff[(r + 1) * g.epr] - s_eoff[r * g.epr];
+            L.rank_tokens[r] = s_rtok[r];
+        }
+    }
+    for (int h = tid; h <= g.H; h += kSmallThreads) {
+        L.host_offset[h] = s_hoff[h];
+        if (h < g.H) {
+            L.host_tokens[h] = s_htok[h];
+            L.relay_dst_rank[h] = h * g.rph + g.s % g.rph;
+        }
+    }
+    if (tid == 0) {
+        L.totals[0] = P;
+        L.totals[1] = s_hoff[g.H];
+        L.totals[2] = s_wmax[0];
+        L.totals[3] = 0;
+    }
+    for (int w = 0; w < kSmallWaves; ++w)
+        for (int e = tid; e < g.E; e += kSmallThreads)
+            s_cnt[w * g.E + e] += s_eoff[e];
+    __syncthreads();
+
+    // ordered walk: rows of each expert in (t, j) order
+    for (int base = pw0; base < pw1; base += kWave) {
+        const int p = base + lane;
+        const bool act = p < pw1;
+        const int e = act ? s_idx[p] : 0;
+        const uint64_t peers = match_peers(act, e, g.nbits);
+        if (act) {
+            const int before = __popcll(peers & below);
+            const int first = s_cnt[wave * g.E + e];
+            const int row = first + before;
+            L.slot[p] = row;
+            L.row_token[row] = g.div_k.div(p);
+            if (before == 0)
+                s_cnt[wave * g.E + e] = first + __popcll(peers);
+        }
+    }
+    if (!g.relay)
+        return;
+    const int o = (tid < g.T ? tid : 0) * g.k;
+    relay_rows(tid < g.T, tid, s_idx + o, s_rk + o, s_hk + o, g,
+               [&](int h) { return s_hoff[h] + s_hcnt[wave * g.H + h]; }, L);
+    clear_relay_tail(g, s_hoff[g.H], 0, 1, kSmallThreads, L);
+}
+
+// LDS bytes of the single-workgroup path, or 0 when the batch is too large for
+// it. (Expert-column scans use threads [0, E) and host-column scans the last
+// wave, so E <= 512 keeps them apart.)
+size_t small_layout_lds(const Geometry &g)
+{
+    if (g.T > kSmallThreads || g.T * g.k > 4096 || g.E > 512)
+        return 0;
+    const size_t ints = 3 * (size_t)g.T * g.k + (size_t)kSmallWaves * g.E + g.E + 1 + g.R + g.H +
+                        (size_t)kSmallWaves * g.H + g.H + 1;
+    const size_t bytes = ints * sizeof(int32_t);
+    return bytes <= 64 * 1024 ? bytes : 0;
 }
 
 }  // namespace
@@ -307,22 +586,34 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
 hipError_t launch_layout(const Geometry &g, const int32_t *idx, const epx_layout &L,
                          hipStream_t stream)
 {
+    const size_t small = small_layout_lds(g);
+    if (small > 0) {
+        hipLaunchKernelGGL(layout_small_kernel, dim3(1), dim3(kSmallThreads), small, stream, idx,
+                           g, L);
+        return hipGetLastError();
+    }
     const int ncol = g.E + g.R + g.H + 1;
-    hipLaunchKernelGGL(layout_count_kernel, dim3(g.G), dim3(256), ncol * sizeof(int32_t), stream,
-                       idx, g, L.workspace);
+    const int kc = g.ct * g.k;
+    const size_t lds_count = (size_t)(ncol + 3 * kc) * sizeof(int32_t);
+    hipLaunchKernelGGL(layout_count_kernel, dim3(g.G), dim3(kCountThreads), lds_count, stream, idx,
+                       g, L.workspace);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
+    const size_t lds_assign = (size_t)(2 * ncol + g.E + 1 + g.H + 1 + 3 * kc) * sizeof(int32_t);
+    if (g.G <= 64) {
+        hipLaunchKernelGGL(layout_assign_kernel<true>, dim3(g.G), dim3(kAssignThreads), lds_assign,
+                           stream, idx, g, (const int32_t *)L.workspace, L);
+        return hipGetLastError();
+    }
     const int cols_per_block = 256 / kWave;
     hipLaunchKernelGGL(layout_scan_kernel, dim3((ncol + cols_per_block - 1) / cols_per_block),
-                       dim3(256), 0, stream, g, L.workspace, L.expert_count, L.rank_tokens,
-                       L.host_tokens, L.totals);
+                       dim3(256), 0, stream, g, L.workspace);
     err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    const size_t lds = (size_t)(2 * g.E + 1 + g.H + 1) * sizeof(int32_t);
-    hipLaunchKernelGGL(layout_assign_kernel, dim3(g.G), dim3(kAssignThreads), lds, stream, idx, g,
-                       (const int32_t *)L.workspace, L);
+    hipLaunchKernelGGL(layout_assign_kernel<false>, dim3(g.G), dim3(kAssignThreads), lds_assign,
+                       stream, idx, g, (const int32_t *)L.workspace, L);
     return hipGetLastError();
 }
 

@@ -98,7 +98,7 @@ enum {
     EPX_L_FANOUT_RANK_MASK,  /* uint32 [C]   bit (rank mod R/H) for each local rank to feed   */
     EPX_L_RELAY_DST_RANK,    /* int32 [H]    same-index GPU: h*(R/H) + my_rank mod (R/H)     */
     EPX_L_TOTALS,            /* int32 [4]    rows, relay rows, max expert count, bad ids      */
-    EPX_L_WORKSPACE,         /* int32 [..]   scratch between the layout kernels               */
+    EPX_L_WORKSPACE,         /* int32 [..]   scratch between the layout kernels (16-B aligned) */
     EPX_LAYOUT_NARRAYS
 };
 

@@ -60,10 +60,10 @@ def test_layout_sizes(epx):
     assert s["relay_token"] == s["fanout_rank_mask"] == 4096 * 2
     assert s["fanout_expert"] == 4096 * 2 * 8
     assert s["totals"] == 4
-    assert s["workspace"] == 64 * (256 + 16 + 2 + 1)
+    assert s["workspace"] == (64 + 1) * (256 + 16 + 2 + 1)     # 64 chunks of 64 tokens, + totals
     p0 = epx.make_problem(0, 2, 16, 4, 2)
     s0 = dict(zip(epx.LAYOUT_FIELDS, epx.epx_layout_sizes(p0)))
-    assert s0["slot"] == 0 and s0["workspace"] == 16 + 4 + 2 + 1
+    assert s0["slot"] == 0 and s0["workspace"] == (4 + 1) * (16 + 4 + 2 + 1)   # columns padded to 4
 
 
 @pytest.mark.parametrize("geom", [
