@@ -29,6 +29,7 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, public specification
+COPY_BYTES = 256 << 20       # size of the calibration copy
 
 
 def algorithmic_bytes(T, k, H, hidden, rows, relay, fp8):
@@ -54,23 +55,89 @@ def algorithmic_bytes(T, k, H, hidden, rows, relay, fp8):
     return {"dispatch": dispatch, "combine": combine, "layout": layout}
 
 
-def kernel_sources_hash():
+KERNEL_SOURCE = {"dispatch_bf16_kernel": "epx_dispatch.hip", "dispatch_fp8_kernel": "epx_dispatch.hip",
+                 "combine_kernel": "epx_combine.hip"}
+
+
+def kernel_sources_hash(kernel: str = "") -> str:
+    """Hash of the source file holding `kernel` (plus the shared internal
+    header); of every kernel source when the kernel is not listed."""
+    csrc = os.path.join(ROOT, "combine_epx_get_amd", "csrc")
+    if kernel in KERNEL_SOURCE:
+        files = [os.path.join(csrc, KERNEL_SOURCE[kernel]), os.path.join(csrc, "epx_internal.h")]
+    else:
+        files = sorted(glob.glob(os.path.join(csrc, "*")))
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "combine_epx_get_amd", "csrc", "*"))):
+    for f in files:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
 
-def load_counter_traffic(kernel: str, workload: str):
-    """HBM traffic per launch from a committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"counters_{kernel}_{workload}.json")
+def load_counter_traffic(kernel: str, tag: str):
+    """HBM traffic per launch from a committed rocprofv3 counter summary for
+    this kernel and workload tag (workload_mode_payload), if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{kernel}_{tag}.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    if d.get("sources_hash") != kernel_sources_hash():
+    if d.get("sources_hash") != kernel_sources_hash(kernel):
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+KERNEL_NAMES = ("dispatch_bf16_kernel", "dispatch_fp8_kernel", "combine_kernel",
+                "layout_small_kernel", "layout_count_kernel", "layout_scan_kernel",
+                "layout_assign_kernel")
+
+
+def ingest_counters(fetch_csv: str, write_csv: str, tag: str, command: str) -> list:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch) of `bench.py --copy-calibration` into per-kernel HBM traffic
+    summaries under profiles/. The calibration copy (COPY_BYTES read and
+    written) fixes the scale from each counter to bytes."""
+    import csv
+
+    def load(path):
+        rows = list(csv.DictReader(open(path)))
+        return {r["Dispatch_Id"]: r for r in rows}
+
+    fetch, write = load(fetch_csv), load(write_csv)
+
+    # the calibration copy: the copy dispatch whose WRITE_SIZE is nearest
+    # COPY_BYTES; the same dispatch id in the FETCH_SIZE run (same sequence)
+    copies = [r for r in write.values() if "copyBuffer" in r["Kernel_Name"]]
+    if not copies:
+        raise SystemExit("calibration copy not found in the counter csv")
+    cw = min(copies, key=lambda r: abs(float(r["Counter_Value"]) * 1024 - COPY_BYTES))
+    cf = fetch[cw["Dispatch_Id"]]
+    if "copyBuffer" not in cf["Kernel_Name"]:
+        raise SystemExit("the two counter runs do not list the same dispatches")
+    f_factor = COPY_BYTES / (float(cf["Counter_Value"]) * 1024)
+    w_factor = COPY_BYTES / (float(cw["Counter_Value"]) * 1024)
+    out = []
+    for kname in KERNEL_NAMES:
+        fv = [float(r["Counter_Value"]) for r in fetch.values() if kname in r["Kernel_Name"]]
+        wv = [float(r["Counter_Value"]) for r in write.values() if kname in r["Kernel_Name"]]
+        if not fv or not wv:
+            continue
+        fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+        d = {"kernel": kname, "workload": tag, "sources_hash": kernel_sources_hash(kname),
+             "command": command,
+             "launches": {"fetch_run": len(fv), "write_run": len(wv)},
+             "fetch_size_kib_per_launch": round(fk, 3), "write_size_kib_per_launch": round(wk, 3),
+             "calibration": {"copy_bytes": COPY_BYTES,
+                             "copy_fetch_size_kib": float(cf["Counter_Value"]),
+                             "copy_write_size_kib": float(cw["Counter_Value"]),
+                             "fetch_factor": round(f_factor, 5), "write_factor": round(w_factor, 5)},
+             "hbm_read_bytes_per_launch": round(fk * 1024 * f_factor),
+             "hbm_write_bytes_per_launch": round(wk * 1024 * w_factor)}
+        d["hbm_bytes_per_launch"] = d["hbm_read_bytes_per_launch"] + d["hbm_write_bytes_per_launch"]
+        path = os.path.join(ROOT, "profiles", f"counters_{kname}_{tag}.json")
+        with open(path, "w") as f:
+            json.dump(d, f, indent=1)
+        out.append(path)
+    return out
 
 
 def cpu_baseline(w, d, min_seconds=12.0, max_reps=64):
@@ -103,7 +170,20 @@ def main(argv=None) -> int:
     ap.add_argument("--dtype", choices=["bf16", "fp8"], default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time spent timing the oracle for the baseline (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/counters_*.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--ingest-command", default="", help="the profiling command, recorded verbatim")
     args = ap.parse_args(argv)
+
+    if args.ingest_counters:
+        w0 = args.workload
+        from combine_epx_get_amd import workloads as W0
+        tag0 = f"{w0}_{args.mode or W0.WORKLOADS[w0].modes[0]}_{args.dtype or W0.WORKLOADS[w0].dtypes[0]}"
+        for pth in ingest_counters(*args.ingest_counters, tag0, args.ingest_command):
+            print(pth)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path has no "
@@ -156,6 +236,16 @@ def main(argv=None) -> int:
         if ev is not None:
             ev[3].record(stream)
 
+    if args.copy_calibration:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give
+        # the scale from counter units to HBM bytes
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -193,7 +283,7 @@ def main(argv=None) -> int:
     dom = max(("dispatch", "combine"), key=lambda n: per_kernel[n]["us"])
     kname = {"dispatch": "dispatch_fp8_kernel" if fp8 else "dispatch_bf16_kernel",
              "combine": "combine_kernel"}[dom]
-    traffic = load_counter_traffic(kname, args.workload)
+    traffic = load_counter_traffic(kname, f"{args.workload}_{mode}_{dtype}")
     roofline = {"bound": "hbm", "kernel": kname,
                 "achieved": round(per_kernel[dom]["GBs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(per_kernel[dom]["frac_peak"], 4), "traffic": traffic,

@@ -176,11 +176,11 @@ __global__ void f32_to_e4m3_kernel(const float *__restrict__ in, uint8_t *__rest
         out[i] = (uint8_t)f32_to_e4m3(in[i]);
 }
 
-// Column slices per token: enough workgroups to cover the GPU (about 2048)
-// when the batch is small; each slice a whole number of `align` chunks.
-int slice_width(int T, int nvec, int align, int max_width)
+// Column slices per token, each a whole number of `align` chunks: at least
+// `target` workgroups in all (small batches need slices to cover the GPU).
+int slice_width(int T, int nvec, int align, int max_width, int target)
 {
-    int want = T >= 2048 ? 1 : (2048 + T - 1) / T;
+    int want = T >= target ? 1 : (target + T - 1) / T;
     int width = (nvec + want - 1) / want;
     width = ((width + align - 1) / align) * align;
     if (width < 4 * align && nvec > 4 * align)
@@ -198,7 +198,7 @@ hipError_t launch_dispatch_bf16(const Geometry &g, const epx_layout &L, const vo
     const int32_t *dest = g.relay ? L.relay_slot : L.slot;
     const int D = g.relay ? g.H : g.k;
     const int nvec = hidden / 8;
-    const int slice = slice_width(g.T, nvec, kWave, 1 << 30);
+    const int slice = slice_width(g.T, nvec, kWave, 1 << 30, 2048);
     const dim3 grid(g.T, (nvec + slice - 1) / slice);
     hipLaunchKernelGGL(dispatch_bf16_kernel, grid, dim3(kThreads), 0, stream, (const u32x4 *)x,
                        nvec, slice, dest, D, (u32x4 *)recv, (const int32_t *)L.totals);
@@ -211,7 +211,11 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const epx_layout &L, const voi
     const int32_t *dest = g.relay ? L.relay_slot : L.slot;
     const int D = g.relay ? g.H : g.k;
     const int nvec = hidden / 8;          // multiple of 16 (hidden % 128 == 0)
-    const int slice = slice_width(g.T, nvec, 16, kMaxSliceVec);
+    // The fp8 workgroup quantises before it stores, so it needs more,
+    // smaller workgroups to overlap the two: about 2048 * D per batch
+    // (measured on MI355X: 2 slices for 4 relay rows per token at T = 4096,
+    // 4 slices for 8 per-expert rows).
+    const int slice = slice_width(g.T, nvec, 16, kMaxSliceVec, 2048 * D);
     const dim3 grid(g.T, (nvec + slice - 1) / slice);
     const size_t lds = (size_t)slice * 8 + (size_t)(slice / 16) * sizeof(float);
     hipLaunchKernelGGL(dispatch_fp8_kernel, grid, dim3(kThreads), lds, stream, (const u32x4 *)x,

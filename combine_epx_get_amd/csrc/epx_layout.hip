@@ -18,7 +18,7 @@
 //
 // Three shapes, no global atomics and no zero-filled buffers:
 //   small batches (<= 4096 pairs): one workgroup does everything in LDS;
-//   up to 64 workgroups of up to 64 tokens: count, then assign (each assign
+//   up to 16 workgroups of up to 64 tokens: count, then assign (each assign
 //     workgroup sums the count columns itself);
 //   more: count, a column scan (one wave per counter), assign.
 // Every per-pair rank and host is computed once, with division constants
@@ -77,6 +77,8 @@ __device__ __forceinline__ void stage_pairs(const int32_t *__restrict__ idx, int
     }
 }
 
+constexpr int kRegK = 16;   // top-k up to which a token's pairs are handled in registers
+
 // For pair p of a staged chunk (token-major, k per token): count the expert,
 // and the pair's rank / host when no earlier pair of the same token has it.
 __device__ __forceinline__ void count_pair(int p, const Geometry &g, const int32_t *s_idx,
@@ -91,11 +93,22 @@ __device__ __forceinline__ void count_pair(int p, const Geometry &g, const int32
     }
     atomicAdd(&s_hist[s_idx[p]], 1);
     const int first = g.div_k.div(p) * g.k;   // first pair of the token
+    const int jp = p - first;
     const int h = s_hk[p];
     bool new_rank = true, new_host = true;
-    for (int q = first; q < p; ++q) {
-        new_rank = new_rank && s_rk[q] != r;
-        new_host = new_host && s_hk[q] != h;
+    if (g.k <= kRegK) {
+        // independent loads, issued together
+#pragma unroll
+        for (int q = 0; q < kRegK - 1; ++q)
+            if (q < jp) {
+                new_rank = new_rank && s_rk[first + q] != r;
+                new_host = new_host && s_hk[first + q] != h;
+            }
+    } else {
+        for (int q = first; q < p; ++q) {
+            new_rank = new_rank && s_rk[q] != r;
+            new_host = new_host && s_hk[q] != h;
+        }
     }
     if (new_rank)
         atomicAdd(&s_rtok[r], 1);
@@ -105,17 +118,31 @@ __device__ __forceinline__ void count_pair(int p, const Geometry &g, const int32
 
 // Relay rows of one token on one lane of a wave holding up to 64 consecutive
 // tokens: for each host, rows of the tokens that touch it, in token order,
-// from `base(h)` on. Every lane of the wave must call it (ballots).
-template <typename Base>
+// from `base(h)` on. Every lane of the wave must call it (ballots). KR > 0:
+// the token's ids, ranks and hosts are held in registers (k <= KR).
+template <int KR, typename Base>
 __device__ __forceinline__ void relay_rows(bool act, int t, const int32_t *ids, const int32_t *rks,
                                            const int32_t *hks, const Geometry &g, Base base,
                                            const epx_layout &L)
 {
     const uint64_t below = (1ull << lane_id()) - 1ull;
+    constexpr int N = KR > 0 ? KR : 1;
+    int e_[N], r_[N], h_[N];
     uint64_t hosts = 0;
-    if (act)
+    if (KR > 0) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const bool v = act && j < g.k;
+            e_[j] = v ? ids[j] : -1;
+            r_[j] = v ? rks[j] : 0;
+            h_[j] = v ? hks[j] : -1;
+            if (v)
+                hosts |= 1ull << h_[j];
+        }
+    } else if (act) {
         for (int j = 0; j < g.k; ++j)
             hosts |= 1ull << hks[j];
+    }
     for (int h = 0; h < g.H; ++h) {
         const bool has = (hosts >> h) & 1ull;
         const uint64_t bal = __ballot(has);
@@ -128,15 +155,38 @@ __device__ __forceinline__ void relay_rows(bool act, int t, const int32_t *ids, 
         const int r = base(h) + __popcll(bal & below);
         L.relay_slot[(int64_t)t * g.H + h] = r;
         L.relay_token[r] = t;
+        int32_t *fan = L.fanout_expert + (int64_t)r * g.k;
         uint32_t mask = 0;
-        for (int j = 0; j < g.k; ++j) {
-            const bool here = hks[j] == h;
-            L.fanout_expert[(int64_t)r * g.k + j] = here ? ids[j] : -1;
-            if (here)
-                mask |= 1u << (rks[j] - h * g.rph);
+        if (KR > 0) {
+#pragma unroll
+            for (int j = 0; j < N; ++j)
+                if (j < g.k) {
+                    const bool here = h_[j] == h;
+                    fan[j] = here ? e_[j] : -1;
+                    if (here)
+                        mask |= 1u << (r_[j] - h * g.rph);
+                }
+        } else {
+            for (int j = 0; j < g.k; ++j) {
+                const bool here = hks[j] == h;
+                fan[j] = here ? ids[j] : -1;
+                if (here)
+                    mask |= 1u << (rks[j] - h * g.rph);
+            }
         }
         L.fanout_rank_mask[r] = mask;
     }
+}
+
+template <typename Base>
+__device__ __forceinline__ void relay_rows_any(bool act, int t, const int32_t *ids,
+                                               const int32_t *rks, const int32_t *hks,
+                                               const Geometry &g, Base base, const epx_layout &L)
+{
+    if (g.k <= kRegK)
+        relay_rows<kRegK>(act, t, ids, rks, hks, g, base, L);
+    else
+        relay_rows<0>(act, t, ids, rks, hks, g, base, L);
 }
 
 // Relay rows past the used ones, [used, capacity) split over `parts`, read as empty.
@@ -264,11 +314,15 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
 
     stage_pairs(idx, p0, nt * g.k, g, s_idx, s_rk, s_hk, kAssignThreads);
     if (SUMS) {
-        // each thread sums whole columns as 16-byte vectors (Gs % 4 == 0)
+        // each thread sums whole columns as 16-byte vectors (Gs % 4 == 0);
+        // G <= 16 here, so a column is at most 4 vectors, all loaded at once
         for (int c = tid; c < ncol; c += kAssignThreads) {
             const int4 *col = (const int4 *)(ws + (int64_t)c * g.Gs);
             int tot = 0, pre = 0;
-            for (int i = 0; i < g.Gs / 4; ++i) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (4 * i >= g.Gs)
+                    break;
                 const int4 v = col[i];
                 const int i0 = 4 * i;   // entries [G, Gs) are padding, never written
                 tot += (i0 < g.G ? v.x : 0) + (i0 + 1 < g.G ? v.y : 0) +
@@ -361,7 +415,7 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
         }
     } else if (g.relay) {
         const int o = lane * g.k;
-        relay_rows(lane < nt, t0 + lane, s_idx + o, s_rk + o, s_hk + o, g,
+        relay_rows_any(lane < nt, t0 + lane, s_idx + o, s_rk + o, s_hk + o, g,
                    [&](int h) { return s_hoff[h] + s_pre[g.E + g.R + h]; }, L);
     }
     if (g.relay)
@@ -563,7 +617,7 @@ __global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
     if (!g.relay)
         return;
     const int o = (tid < g.T ? tid : 0) * g.k;
-    relay_rows(tid < g.T, tid, s_idx + o, s_rk + o, s_hk + o, g,
+    relay_rows_any(tid < g.T, tid, s_idx + o, s_rk + o, s_hk + o, g,
                [&](int h) { return s_hoff[h] + s_hcnt[wave * g.H + h]; }, L);
     clear_relay_tail(g, s_hoff[g.H], 0, 1, kSmallThreads, L);
 }
@@ -601,7 +655,7 @@ hipError_t launch_layout(const Geometry &g, const int32_t *idx, const epx_layout
     if (err != hipSuccess)
         return err;
     const size_t lds_assign = (size_t)(2 * ncol + g.E + 1 + g.H + 1 + 3 * kc) * sizeof(int32_t);
-    if (g.G <= 64) {
+    if (g.G <= 16) {
         hipLaunchKernelGGL(layout_assign_kernel<true>, dim3(g.G), dim3(kAssignThreads), lds_assign,
                            stream, idx, g, (const int32_t *)L.workspace, L);
         return hipGetLastError();
