@@ -18,6 +18,11 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
   dispatch_fp8   -- converter exhaustive vs torch's float8_e4m3fn cast; block
                     properties (amax code is 448, error bound of a 3-bit mantissa).
   combine        -- float64 sum within the float32 error bound; exact special cases.
+  relay_fanout   -- equals the per-expert dispatch row for row (two independent
+                    definitions); membership by host brute force.
+  relay_partials / relay_finish -- one host reduces to the flat combine bit for
+                    bit; partial membership by exact power-of-two tagging;
+                    float64 sum within the float32 bound.
   relay row order, zero-block rule, fma order: parity unpinned by the pages
                     (fixed by the readings recorded in the design notes).
 """
@@ -65,6 +70,12 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.oracle_dispatch_fp8.restype = ctypes.c_int
     lib.oracle_combine.argtypes = [i32] * 3 + [P] * 4
     lib.oracle_combine.restype = ctypes.c_int
+    lib.oracle_relay_fanout.argtypes = [i32] * 5 + [ctypes.c_int64, i32] + [P] * 7
+    lib.oracle_relay_fanout.restype = ctypes.c_int
+    lib.oracle_relay_partials.argtypes = [i32] * 7 + [P] * 6
+    lib.oracle_relay_partials.restype = ctypes.c_int
+    lib.oracle_relay_finish.argtypes = [i32] * 4 + [P] * 3
+    lib.oracle_relay_finish.restype = ctypes.c_int
     for name in ("oracle_f32_to_e4m3_array", "oracle_f32_to_bf16_array", "oracle_e4m3_to_f32_array"):
         getattr(lib, name).argtypes = [P, P, ctypes.c_int64]
         getattr(lib, name).restype = None
@@ -165,6 +176,61 @@ def combine(y_bits: np.ndarray, lay: dict, topk_weights: np.ndarray, lib=None) -
     rc = lib.oracle_combine(T, k, hidden, _p(lay["slot"]), _p(w), _p(y), _p(out))
     if rc != 0:
         raise OracleError(rc, "oracle_combine")
+    return out
+
+
+def relay_fanout(relay_rows: np.ndarray, lay: dict, topk_idx: np.ndarray, num_experts: int,
+                 num_ranks: int, num_hosts: int, relay_scales: Optional[np.ndarray] = None,
+                 lib=None):
+    """Per-expert rows [T*k, ...] (same dtype as relay_rows) built from relay
+    rows by the fan-out definition; with relay_scales also the scales."""
+    lib = lib or load()
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, k = idx.shape
+    rows = np.ascontiguousarray(relay_rows)
+    row_bytes = rows.shape[1] * rows.itemsize
+    recv = np.zeros((T * k,) + rows.shape[1:], rows.dtype)
+    nsc = 0 if relay_scales is None else relay_scales.shape[1]
+    sc_in = np.ascontiguousarray(relay_scales if relay_scales is not None else np.zeros((1, 1), np.float32),
+                                 dtype=np.float32)
+    sc_out = np.zeros((T * k, max(nsc, 1)), np.float32)
+    rc = lib.oracle_relay_fanout(T, k, num_experts, num_ranks, num_hosts, row_bytes, nsc, _p(idx),
+                                 _p(lay["slot"]), _p(lay["relay_slot"]), _p(rows), _p(sc_in), _p(recv),
+                                 _p(sc_out))
+    if rc != 0:
+        raise OracleError(rc, "oracle_relay_fanout")
+    return (recv, sc_out[:, :nsc]) if relay_scales is not None else recv
+
+
+def relay_partials(y_bits: np.ndarray, lay: dict, topk_idx: np.ndarray, topk_weights: np.ndarray,
+                   num_experts: int, num_ranks: int, num_hosts: int, bf16: bool = False, lib=None):
+    """Per relay row fp32 (or bf16-bit) partial sums [relay_rows, h]."""
+    lib = lib or load()
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, k = idx.shape
+    y = np.ascontiguousarray(y_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(topk_weights, dtype=np.float32)
+    hidden = y.shape[1]
+    rows = int(lay["totals"][1])
+    part = np.zeros((rows, hidden), np.uint16 if bf16 else np.float32)
+    rc = lib.oracle_relay_partials(T, k, num_experts, num_ranks, num_hosts, hidden, int(bf16), _p(idx),
+                                   _p(lay["slot"]), _p(lay["relay_slot"]), _p(w), _p(y), _p(part))
+    if rc != 0:
+        raise OracleError(rc, "oracle_relay_partials")
+    return part
+
+
+def relay_finish(partials: np.ndarray, lay: dict, num_tokens: int, num_hosts: int, lib=None) -> np.ndarray:
+    """out [T, h] bf16 bits from the per-host partials."""
+    lib = lib or load()
+    part = np.ascontiguousarray(partials)
+    bf16 = part.dtype == np.uint16
+    hidden = part.shape[1]
+    out = np.zeros((num_tokens, hidden), np.uint16)
+    rc = lib.oracle_relay_finish(num_tokens, num_hosts, hidden, int(bf16), _p(lay["relay_slot"]), _p(part),
+                                 _p(out))
+    if rc != 0:
+        raise OracleError(rc, "oracle_relay_finish")
     return out
 
 

@@ -458,3 +458,106 @@ int oracle_combine(int32_t T, int32_t k, int32_t hidden, const int32_t *slot,
         }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* Relay receive side and two-level combine                            */
+/* ------------------------------------------------------------------ */
+/*
+ * Mode 2 of the digest (section 3.2, Figure 3): the relayed copy of a token
+ * arrives once at the same-index GPU of each destination host and is fanned
+ * out there to the token's experts on that host; on the way back that GPU
+ * sums its experts' results before sending one partial back, and the source
+ * sums the partials of the hosts.
+ */
+
+/* Fan-out of relay rows (row_bytes bytes each, plus nsc float32 scales when
+ * nsc > 0): for every token t and host h with a relay row r, and every j
+ * whose expert idx[t,j] sits on host h, per-expert row slot[t,j] = row r. */
+int oracle_relay_fanout(int32_t T, int32_t k, int32_t E, int32_t R, int32_t H,
+                        int64_t row_bytes, int32_t nsc, const int32_t *idx,
+                        const int32_t *slot, const int32_t *relay_slot,
+                        const uint8_t *relay_rows, const float *relay_scales,
+                        uint8_t *recv, float *recv_scales)
+{
+    if (!geometry_ok(T, k, E, R, H, 0) || row_bytes < 1 || nsc < 0)
+        return ORC_ERR_ARG;
+    const int32_t epr = E / R, rph = R / H;
+    for (int32_t t = 0; t < T; ++t)
+        for (int32_t h = 0; h < H; ++h) {
+            int32_t r = relay_slot[(int64_t)t * H + h];
+            if (r < 0)
+                continue;
+            for (int32_t j = 0; j < k; ++j) {
+                int32_t e = idx[(int64_t)t * k + j];
+                if (e < 0 || e >= E)
+                    return ORC_ERR_INDEX;
+                if (host_of(e, epr, rph) != h)
+                    continue;
+                int64_t dst = slot[(int64_t)t * k + j];
+                for (int64_t b = 0; b < row_bytes; ++b)
+                    recv[dst * row_bytes + b] = relay_rows[(int64_t)r * row_bytes + b];
+                for (int32_t q = 0; q < nsc; ++q)
+                    recv_scales[dst * nsc + q] = relay_scales[(int64_t)r * nsc + q];
+            }
+        }
+    return ORC_OK;
+}
+
+/* Level 1 (relay GPU): for relay row r = (t, h), partial[r, c] = sum over j
+ * ascending with host(idx[t,j]) == h of w[t,j] * y[slot[t,j], c], in float32
+ * as acc = fmaf(w, y, acc) from +0. Stored as float32 (bf16_out == 0) or
+ * rounded to bf16 (bf16_out != 0; partials then hold uint16 patterns). */
+int oracle_relay_partials(int32_t T, int32_t k, int32_t E, int32_t R, int32_t H,
+                          int32_t hidden, int32_t bf16_out, const int32_t *idx,
+                          const int32_t *slot, const int32_t *relay_slot, const float *w,
+                          const uint16_t *y, void *partials)
+{
+    if (!geometry_ok(T, k, E, R, H, 0) || hidden < 1)
+        return ORC_ERR_ARG;
+    const int32_t epr = E / R, rph = R / H;
+    for (int32_t t = 0; t < T; ++t)
+        for (int32_t h = 0; h < H; ++h) {
+            int32_t r = relay_slot[(int64_t)t * H + h];
+            if (r < 0)
+                continue;
+            for (int32_t c = 0; c < hidden; ++c) {
+                float acc = 0.0f;
+                for (int32_t j = 0; j < k; ++j) {
+                    int32_t e = idx[(int64_t)t * k + j];
+                    if (host_of(e, epr, rph) != h)
+                        continue;
+                    int32_t row = slot[(int64_t)t * k + j];
+                    acc = fmaf(w[(int64_t)t * k + j], oracle_bf16_to_f32(y[(int64_t)row * hidden + c]),
+                               acc);
+                }
+                if (bf16_out)
+                    ((uint16_t *)partials)[(int64_t)r * hidden + c] = oracle_f32_to_bf16(acc);
+                else
+                    ((float *)partials)[(int64_t)r * hidden + c] = acc;
+            }
+        }
+    return ORC_OK;
+}
+
+/* Level 2 (source): out[t, c] = bf16( sum over h ascending of partial of
+ * relay row relay_slot[t, h] (where it exists) ), float32 adds from +0. */
+int oracle_relay_finish(int32_t T, int32_t H, int32_t hidden, int32_t bf16_in,
+                        const int32_t *relay_slot, const void *partials, uint16_t *out)
+{
+    if (T < 0 || H < 1 || hidden < 1)
+        return ORC_ERR_ARG;
+    for (int32_t t = 0; t < T; ++t)
+        for (int32_t c = 0; c < hidden; ++c) {
+            float acc = 0.0f;
+            for (int32_t h = 0; h < H; ++h) {
+                int32_t r = relay_slot[(int64_t)t * H + h];
+                if (r < 0)
+                    continue;
+                float p = bf16_in ? oracle_bf16_to_f32(((const uint16_t *)partials)[(int64_t)r * hidden + c])
+                                  : ((const float *)partials)[(int64_t)r * hidden + c];
+                acc = acc + p;
+            }
+            out[(int64_t)t * hidden + c] = oracle_f32_to_bf16(acc);
+        }
+    return ORC_OK;
+}

@@ -18,6 +18,7 @@ import pytest
 import oracle
 from tests import test_oracle_layout as TL
 from tests import test_oracle_numerics as TN
+from tests import test_oracle_relay as TRL
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "epx_oracle.c")
 
@@ -80,6 +81,18 @@ MUTANTS = [
     ("combine transposes the weights",
      "                acc = fmaf(w[(int64_t)t * k + j], v, acc);",
      "                acc = fmaf(w[((int64_t)j * T + t) % ((int64_t)T * k)], v, acc);"),
+    ("fan-out compares the rank with the host",
+     "                if (host_of(e, epr, rph) != h)\n                    continue;\n                int64_t dst",
+     "                if (rank_of(e, epr) != h)\n                    continue;\n                int64_t dst"),
+    ("partials drop the last expert",
+     "                for (int32_t j = 0; j < k; ++j) {\n                    int32_t e = idx[(int64_t)t * k + j];\n                    if (host_of(e, epr, rph) != h)",
+     "                for (int32_t j = 0; j + 1 < k; ++j) {\n                    int32_t e = idx[(int64_t)t * k + j];\n                    if (host_of(e, epr, rph) != h)"),
+    ("partials take the next weight",
+     "                    acc = fmaf(w[(int64_t)t * k + j], oracle_bf16_to_f32(y[(int64_t)row * hidden + c]),",
+     "                    acc = fmaf(w[(int64_t)t * k + (j + 1) % k], oracle_bf16_to_f32(y[(int64_t)row * hidden + c]),"),
+    ("finish reads the first host only",
+     "                int32_t r = relay_slot[(int64_t)t * H + h];\n                if (r < 0)\n                    continue;\n                float p",
+     "                int32_t r = relay_slot[(int64_t)t * H];\n                if (r < 0)\n                    continue;\n                float p"),
     ("combine subtracts",
      "                acc = fmaf(w[(int64_t)t * k + j], v, acc);",
      "                acc = fmaf(-w[(int64_t)t * k + j], v, acc);"),
@@ -109,6 +122,12 @@ def _pins():
     calls.append(TN.test_combine_exact_special_cases)
     calls.append(TN.test_combine_identity_experts_return_x)
     calls.append(TN.test_combine_config_rule_closed_form)
+    for shape in TRL.SHAPES:
+        calls.append(lambda sh=shape: TRL.test_fanout_of_tagged_rows_brute_force(sh))
+        calls.append(lambda sh=shape: TRL.test_partial_membership_exact(sh))
+    calls.append(lambda: TRL.test_fanout_of_relay_dispatch_is_per_expert_dispatch(TRL.SHAPES[1]))
+    calls.append(lambda: TRL.test_one_host_two_level_is_flat(8, 256, 32))
+    calls.append(lambda: TRL.test_two_level_within_bounds_of_float64(TRL.SHAPES[1]))
     return calls
 
 
