@@ -56,7 +56,24 @@ def algorithmic_bytes(T, k, H, hidden, rows, relay, fp8):
 
 
 KERNEL_SOURCE = {"dispatch_bf16_kernel": "epx_dispatch.hip", "dispatch_fp8_kernel": "epx_dispatch.hip",
-                 "combine_kernel": "epx_combine.hip"}
+                 "combine_kernel": "epx_combine.hip", "relay_fanout_kernel": "epx_relay.hip",
+                 "relay_partials_kernel": "epx_relay.hip", "relay_finish_kernel": "epx_relay.hip"}
+
+
+def relay_receive_bytes(T, k, H, hidden, rows, fp8, f32_partials):
+    """Algorithmic bytes of the relay receive side and the two-level combine.
+
+    fan-out:  read the relay rows in use, write the T*k per-expert rows (same
+              payload), read fan-out lists, slots and row tokens.
+    partials: read the T*k expert-output rows (bf16) and slots/weights; write
+              one partial row per relay row in use (fp32 or bf16).
+    finish:   read the partial rows in use and the relay slots, write out.
+    """
+    row = hidden + (hidden // 128) * 4 if fp8 else hidden * 2
+    prow = hidden * (4 if f32_partials else 2)
+    return {"relay_fanout": rows * row + T * k * row + rows * (k + 1) * 4 + T * k * 4,
+            "relay_partials": T * k * hidden * 2 + T * k * 8 + rows * (k + 1) * 4 + rows * prow,
+            "relay_finish": rows * prow + T * H * 4 + T * hidden * 2}
 
 
 def kernel_sources_hash(kernel: str = "") -> str:
@@ -87,6 +104,7 @@ def load_counter_traffic(kernel: str, tag: str):
 
 
 KERNEL_NAMES = ("dispatch_bf16_kernel", "dispatch_fp8_kernel", "combine_kernel",
+                "relay_fanout_kernel", "relay_partials_kernel", "relay_finish_kernel",
                 "layout_small_kernel", "layout_count_kernel", "layout_scan_kernel",
                 "layout_assign_kernel")
 
@@ -170,6 +188,11 @@ def main(argv=None) -> int:
     ap.add_argument("--dtype", choices=["bf16", "fp8"], default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time spent timing the oracle for the baseline (0: skip)")
+    ap.add_argument("--relay-receive", action="store_true",
+                    help="relay mode: step = layout, relay dispatch, fan-out to per-expert rows, "
+                         "per-host partials and the source-side finish (instead of the flat combine)")
+    ap.add_argument("--partials", choices=["f32", "bf16"], default="f32",
+                    help="wire form of the relay partials (with --relay-receive)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -196,7 +219,7 @@ def main(argv=None) -> int:
     from combine_epx_get_amd import workloads as W
 
     w = W.WORKLOADS[args.workload]
-    mode = args.mode or w.modes[0]
+    mode = args.mode or ("relay" if args.relay_receive else w.modes[0])
     dtype = args.dtype or w.dtypes[0]
     relay = mode == "relay"
     fp8 = dtype == "fp8"
@@ -223,6 +246,17 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream()
     out_dtype = epx.FP8_E4M3 if fp8 else epx.BF16
 
+    receive = args.relay_receive
+    if receive:
+        if not relay:
+            print("--relay-receive needs relay mode", file=sys.stderr)
+            return 2
+        # the relay GPU's per-expert rows, its partials (the return wire) and the output
+        fan = torch.empty((T * k, hidden), dtype=recv.dtype, device=dev)
+        fan_sc = torch.empty((T * k, hidden // 128), dtype=torch.float32, device=dev) if fp8 else None
+        part = torch.empty((cap, hidden), dtype=torch.float32 if args.partials == "f32" else torch.bfloat16,
+                           device=dev)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
@@ -232,7 +266,16 @@ def main(argv=None) -> int:
         epx.epx_dispatch(p, L, x, out_dtype, recv, scales, stream)
         if ev is not None:
             ev[2].record(stream)
-        epx.epx_combine(p, L, y, wts, out, stream)
+        if receive:
+            epx.epx_relay_fanout(p, L, recv, fan, scales, fan_sc, stream)
+            if ev is not None:
+                ev[4].record(stream)
+            epx.epx_combine_relay_partials(p, L, y, wts, part, stream)
+            if ev is not None:
+                ev[5].record(stream)
+            epx.epx_combine_relay_finish(p, L, part, out, stream)
+        else:
+            epx.epx_combine(p, L, y, wts, out, stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -253,7 +296,7 @@ def main(argv=None) -> int:
     totals = L["totals"].cpu().numpy()
     rows = int(totals[1] if relay else totals[0])
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -263,11 +306,20 @@ def main(argv=None) -> int:
 
     lay_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     dis_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    com_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    if receive:
+        fan_ms = np.array([e[2].elapsed_time(e[4]) for e in evs])
+        par_ms = np.array([e[4].elapsed_time(e[5]) for e in evs])
+        fin_ms = np.array([e[5].elapsed_time(e[3]) for e in evs])
+        com_ms = par_ms + fin_ms
+    else:
+        com_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
     step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
     ms_per_step = wall * 1e3 / args.steps
 
     nbytes = algorithmic_bytes(T, k, w.num_hosts, hidden, rows, relay, fp8)
+    if receive:
+        nbytes.update(relay_receive_bytes(T, k, w.num_hosts, hidden, rows, fp8, args.partials == "f32"))
+        del nbytes["combine"]
     layer_bytes = sum(nbytes.values())
     us_layer = float(step_ms.mean() * 1e3)
     value = layer_bytes / (ms_per_step * 1e-3) / 1e9
@@ -275,14 +327,20 @@ def main(argv=None) -> int:
     per_kernel = {
         "layout": {"us": float(lay_ms.mean() * 1e3), "bytes": nbytes["layout"]},
         "dispatch": {"us": float(dis_ms.mean() * 1e3), "bytes": nbytes["dispatch"]},
-        "combine": {"us": float(com_ms.mean() * 1e3), "bytes": nbytes["combine"]},
     }
+    if receive:
+        per_kernel["relay_fanout"] = {"us": float(fan_ms.mean() * 1e3), "bytes": nbytes["relay_fanout"]}
+        per_kernel["relay_partials"] = {"us": float(par_ms.mean() * 1e3), "bytes": nbytes["relay_partials"]}
+        per_kernel["relay_finish"] = {"us": float(fin_ms.mean() * 1e3), "bytes": nbytes["relay_finish"]}
+    else:
+        per_kernel["combine"] = {"us": float(com_ms.mean() * 1e3), "bytes": nbytes["combine"]}
     for v in per_kernel.values():
         v["GBs"] = v["bytes"] / (v["us"] * 1e-6) / 1e9
         v["frac_peak"] = v["GBs"] / PEAK_HBM_GBS
-    dom = max(("dispatch", "combine"), key=lambda n: per_kernel[n]["us"])
+    dom = max((n for n in per_kernel if n != "layout"), key=lambda n: per_kernel[n]["us"])
     kname = {"dispatch": "dispatch_fp8_kernel" if fp8 else "dispatch_bf16_kernel",
-             "combine": "combine_kernel"}[dom]
+             "combine": "combine_kernel", "relay_fanout": "relay_fanout_kernel",
+             "relay_partials": "relay_partials_kernel", "relay_finish": "relay_finish_kernel"}[dom]
     traffic = load_counter_traffic(kname, f"{args.workload}_{mode}_{dtype}")
     roofline = {"bound": "hbm", "kernel": kname,
                 "achieved": round(per_kernel[dom]["GBs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -307,7 +365,8 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens": T, "hidden": hidden, "experts": w.num_experts,
                    "topk": k, "ranks": w.num_ranks, "hosts": w.num_hosts, "routing": w.routing,
-                   "mode": mode, "payload": dtype},
+                   "mode": mode + ("+receive" if receive else ""), "payload": dtype,
+                   **({"partials": args.partials} if receive else {})},
         "us_per_layer": round(us_layer, 2),
         "pct_of_peak_layer": round(100 * layer_bytes / (us_layer * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
         "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}

@@ -199,6 +199,89 @@ epx_status epx_combine(const epx_problem *p, const epx_layout *layout, const voi
         epx::launch_combine(g, *layout, y, topk_weights, hidden, out, (hipStream_t)stream));
 }
 
+epx_status epx_relay_fanout(const epx_problem *p, const epx_layout *layout,
+                            const void *relay_rows, const float *relay_scales,
+                            int64_t relay_capacity_rows, int32_t hidden, int32_t dtype,
+                            void *recv, float *recv_scales, int64_t capacity_rows, void *stream)
+{
+    Geometry g;
+    epx_status st = make_geometry(p, &g);
+    if (st != EPX_OK)
+        return st;
+    if (!g.relay)
+        return EPX_ERR_ARG;
+    if ((st = check_layout(g, layout)) != EPX_OK)
+        return st;
+    if (dtype != EPX_BF16 && dtype != EPX_FP8_E4M3)
+        return EPX_ERR_ARG;
+    if (hidden < 8 || hidden % 8 != 0 || (dtype == EPX_FP8_E4M3 && hidden % epx::kFp8Block != 0))
+        return EPX_ERR_ARG;
+    if (relay_capacity_rows < relay_capacity(g) || capacity_rows < (int64_t)g.T * g.k)
+        return EPX_ERR_CAPACITY;
+    if (g.T == 0)
+        return EPX_OK;
+    if (!relay_rows || !recv || !aligned(relay_rows, 16) || !aligned(recv, 16))
+        return EPX_ERR_ARG;
+    const bool fp8 = dtype == EPX_FP8_E4M3;
+    if (fp8 && (!relay_scales || !recv_scales || !aligned(relay_scales, 4) || !aligned(recv_scales, 4)))
+        return EPX_ERR_ARG;
+    const int64_t row_bytes = fp8 ? hidden : (int64_t)hidden * 2;
+    return from_hip(epx::launch_relay_fanout(g, *layout, relay_rows, relay_scales, row_bytes,
+                                             fp8 ? hidden / epx::kFp8Block : 0, recv, recv_scales,
+                                             (hipStream_t)stream));
+}
+
+epx_status epx_combine_relay_partials(const epx_problem *p, const epx_layout *layout,
+                                      const void *y, int64_t y_rows, const float *topk_weights,
+                                      int32_t hidden, int32_t partial_dtype, void *partials,
+                                      int64_t partial_capacity_rows, void *stream)
+{
+    Geometry g;
+    epx_status st = make_geometry(p, &g);
+    if (st != EPX_OK)
+        return st;
+    if (!g.relay)
+        return EPX_ERR_ARG;
+    if ((st = check_layout(g, layout)) != EPX_OK)
+        return st;
+    if ((partial_dtype != EPX_F32 && partial_dtype != EPX_BF16) || hidden < 8 || hidden % 8 != 0)
+        return EPX_ERR_ARG;
+    if (y_rows < (int64_t)g.T * g.k || partial_capacity_rows < relay_capacity(g))
+        return EPX_ERR_CAPACITY;
+    if (g.T == 0)
+        return EPX_OK;
+    if (!y || !topk_weights || !partials || !aligned(y, 16) || !aligned(topk_weights, 4) ||
+        !aligned(partials, 16))
+        return EPX_ERR_ARG;
+    return from_hip(epx::launch_relay_partials(g, *layout, y, topk_weights, hidden,
+                                               partial_dtype == EPX_BF16, partials,
+                                               (hipStream_t)stream));
+}
+
+epx_status epx_combine_relay_finish(const epx_problem *p, const epx_layout *layout,
+                                    const void *partials, int64_t partial_capacity_rows,
+                                    int32_t partial_dtype, int32_t hidden, void *out, void *stream)
+{
+    Geometry g;
+    epx_status st = make_geometry(p, &g);
+    if (st != EPX_OK)
+        return st;
+    if (!g.relay)
+        return EPX_ERR_ARG;
+    if ((st = check_layout(g, layout)) != EPX_OK)
+        return st;
+    if ((partial_dtype != EPX_F32 && partial_dtype != EPX_BF16) || hidden < 8 || hidden % 8 != 0)
+        return EPX_ERR_ARG;
+    if (partial_capacity_rows < relay_capacity(g))
+        return EPX_ERR_CAPACITY;
+    if (g.T == 0)
+        return EPX_OK;
+    if (!partials || !out || !aligned(partials, 16) || !aligned(out, 16))
+        return EPX_ERR_ARG;
+    return from_hip(epx::launch_relay_finish(g, *layout, partials, partial_dtype == EPX_BF16,
+                                             hidden, out, (hipStream_t)stream));
+}
+
 epx_status epx_read_error(const epx_layout *layout, int32_t *bad_count, void *stream)
 {
     if (!layout || !layout->totals)

@@ -61,5 +61,13 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const epx_layout &L, const voi
 hipError_t launch_combine(const Geometry &g, const epx_layout &L, const void *y,
                           const float *w, int32_t hidden, void *out, hipStream_t stream);
 hipError_t launch_f32_to_e4m3(const float *in, uint8_t *out, int64_t n, hipStream_t stream);
+hipError_t launch_relay_fanout(const Geometry &g, const epx_layout &L, const void *relay_rows,
+                               const float *relay_scales, int64_t row_bytes, int nsc,
+                               void *recv, float *recv_scales, hipStream_t stream);
+hipError_t launch_relay_partials(const Geometry &g, const epx_layout &L, const void *y,
+                                 const float *w, int32_t hidden, bool bf16_out, void *partials,
+                                 hipStream_t stream);
+hipError_t launch_relay_finish(const Geometry &g, const epx_layout &L, const void *partials,
+                               bool bf16_in, int32_t hidden, void *out, hipStream_t stream);
 
 }  // namespace epx

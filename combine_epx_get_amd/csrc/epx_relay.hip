@@ -1,0 +1,287 @@
+// epx_relay.hip -- receive side of the host relay and the two-level combine.
+//
+// Mode 2 of the digest "Balancing and Beyond: Communication-Centric
+// Optimizations in Expert Parallelism" (section 3.2, Figure 3): a token's
+// copy crosses to the same-index GPU of each destination host once and is
+// fanned out there to the token's experts on that host; on the way back that
+// GPU sums its experts' results and returns one partial per token, which the
+// source sums over the hosts.
+//
+//   relay_fanout:   relay row r -> per-expert rows slot[t, j] of every j with
+//                   fanout_expert[r, j] >= 0 (bf16 rows, or fp8 codes +
+//                   scales); one workgroup reads the row once and its waves
+//                   stream whole destination rows.
+//   relay_partials: relay row r = (t, h) -> partial[r] = sum over those j,
+//                   ascending, of w[t, j] * y[slot[t, j]] in fp32 fma from +0,
+//                   stored as fp32 or rounded to bf16 (the return wire form).
+//   relay_finish:   out[t] = bf16(sum over h ascending of partial[relay_slot[t, h]]),
+//                   fp32 adds from +0.
+//
+// All three are HBM-bound gathers/scatters like dispatch and combine. Relay
+// rows are visited up to the row capacity; workgroups past totals[1] (the
+// rows in use) return at once.
+#include "epx_internal.h"
+
+namespace epx {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kBurst = 4;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return ((u >> 16) & 0x8000u) | 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// The fan-out list of relay row r in ascending j: (destination slot, j).
+// Returns its length; s_dst / s_j hold up to k entries. Every thread calls it.
+__device__ __forceinline__ int fanout_list(const epx_layout &L, int k, int64_t r, int t,
+                                           int32_t *s_dst, int32_t *s_j, int32_t *s_n)
+{
+    if (threadIdx.x < kWave) {
+        // k <= 64: one lane per j, compacted in j order with a ballot prefix
+        const int j = threadIdx.x;
+        const bool on = j < k && L.fanout_expert[r * k + j] >= 0;
+        const uint64_t bal = __ballot(on);
+        if (on) {
+            const int pos = __popcll(bal & ((1ull << j) - 1ull));
+            s_dst[pos] = L.slot[(int64_t)t * k + j];
+            s_j[pos] = j;
+        }
+        if (j == 0)
+            *s_n = __popcll(bal);
+    }
+    __syncthreads();
+    return *s_n;
+}
+
+// Rows are row_vec 16-byte vectors; nsc float32 scales per row (fp8) or 0.
+__global__ __launch_bounds__(kThreads) void relay_fanout_kernel(
+    const u32x4 *__restrict__ src, const float *__restrict__ src_sc, int row_vec, int nsc,
+    int slice, int k, epx_layout L, u32x4 *__restrict__ dst, float *__restrict__ dst_sc)
+{
+    __shared__ int32_t s_dst[kMaxTopk], s_j[kMaxTopk], s_n;
+    if (L.totals[3] != 0)
+        return;
+    const int64_t r = blockIdx.x;
+    if (r >= L.totals[1])
+        return;   // past the relay rows in use
+    const int t = L.relay_token[r];
+    const int n = fanout_list(L, k, r, t, s_dst, s_j, &s_n);
+    const int c_beg = blockIdx.y * slice;
+    const int c_end = min(row_vec, c_beg + slice);
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const u32x4 *row = src + r * row_vec;
+    for (int d = wave; d < n; d += kWaves) {
+        const int64_t o = s_dst[d];
+        u32x4 *out = dst + o * row_vec;
+        for (int c0 = c_beg + lane; c0 < c_end; c0 += kWave * kBurst) {
+            u32x4 v[kBurst];
+#pragma unroll
+            for (int i = 0; i < kBurst; ++i) {
+                const int c = c0 + i * kWave;
+                if (c < c_end)
+                    v[i] = row[c];
+            }
+#pragma unroll
+            for (int i = 0; i < kBurst; ++i) {
+                const int c = c0 + i * kWave;
+                if (c < c_end)
+                    __builtin_nontemporal_store(v[i], out + c);
+            }
+        }
+        if (nsc > 0 && blockIdx.y == 0)
+            for (int q = lane; q < nsc; q += kWave)
+                dst_sc[o * nsc + q] = src_sc[r * nsc + q];
+    }
+}
+
+// Partials: lanes own 8 channels (one 16-byte bf16 vector of y); fp32 output
+// is two 16-byte vectors per lane, bf16 one.
+template <bool BF16_OUT>
+__global__ __launch_bounds__(kThreads) void relay_partials_kernel(
+    const u32x4 *__restrict__ y, int nvec, int slice, const float *__restrict__ w, int k,
+    epx_layout L, void *__restrict__ partials)
+{
+    __shared__ int32_t s_dst[kMaxTopk], s_j[kMaxTopk], s_n;
+    __shared__ float s_w[kMaxTopk];
+    if (L.totals[3] != 0)
+        return;
+    const int64_t r = blockIdx.x;
+    if (r >= L.totals[1])
+        return;
+    const int t = L.relay_token[r];
+    const int n = fanout_list(L, k, r, t, s_dst, s_j, &s_n);
+    if (threadIdx.x < n)
+        s_w[threadIdx.x] = w[(int64_t)t * k + s_j[threadIdx.x]];
+    __syncthreads();
+    const int c_beg = blockIdx.y * slice;
+    const int c_end = min(nvec, c_beg + slice);
+    for (int c = c_beg + threadIdx.x; c < c_end; c += kThreads) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[i] = 0.0f;
+        for (int j0 = 0; j0 < n; j0 += 8) {
+            u32x4 v[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                if (j0 + jj < n)
+                    v[jj] = __builtin_nontemporal_load(y + (int64_t)s_dst[j0 + jj] * nvec + c);
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                if (j0 + jj >= n)
+                    break;
+                const float wj = s_w[j0 + jj];
+                acc[0] = __builtin_fmaf(wj, bf16_lo(v[jj].x), acc[0]);
+                acc[1] = __builtin_fmaf(wj, bf16_hi(v[jj].x), acc[1]);
+                acc[2] = __builtin_fmaf(wj, bf16_lo(v[jj].y), acc[2]);
+                acc[3] = __builtin_fmaf(wj, bf16_hi(v[jj].y), acc[3]);
+                acc[4] = __builtin_fmaf(wj, bf16_lo(v[jj].z), acc[4]);
+                acc[5] = __builtin_fmaf(wj, bf16_hi(v[jj].z), acc[5]);
+                acc[6] = __builtin_fmaf(wj, bf16_lo(v[jj].w), acc[6]);
+                acc[7] = __builtin_fmaf(wj, bf16_hi(v[jj].w), acc[7]);
+            }
+        }
+        if (BF16_OUT) {
+            u32x4 o;
+            o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+            o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+            o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+            o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+            __builtin_nontemporal_store(o, (u32x4 *)partials + r * nvec + c);
+        } else {
+            u32x4 *o = (u32x4 *)partials + (r * nvec + c) * 2;
+            const u32x4 a = {__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                             __float_as_uint(acc[2]), __float_as_uint(acc[3])};
+            const u32x4 b = {__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                             __float_as_uint(acc[6]), __float_as_uint(acc[7])};
+            __builtin_nontemporal_store(a, o);
+            __builtin_nontemporal_store(b, o + 1);
+        }
+    }
+}
+
+// Finish: lanes own 8 channels of the token's output row.
+template <bool BF16_IN>
+__global__ __launch_bounds__(kThreads) void relay_finish_kernel(
+    const void *__restrict__ partials, int nvec, int slice, int H, epx_layout L,
+    u32x4 *__restrict__ out)
+{
+    __shared__ int32_t s_rows[kMaxHosts], s_n;
+    if (L.totals[3] != 0)
+        return;
+    const int64_t t = blockIdx.x;
+    if (threadIdx.x < kWave) {
+        const int h = threadIdx.x;
+        const int r = h < H ? L.relay_slot[t * H + h] : -1;
+        const uint64_t bal = __ballot(r >= 0);
+        if (r >= 0)
+            s_rows[__popcll(bal & ((1ull << h) - 1ull))] = r;
+        if (h == 0)
+            s_n = __popcll(bal);
+    }
+    __syncthreads();
+    const int n = s_n;
+    const int c_beg = blockIdx.y * slice;
+    const int c_end = min(nvec, c_beg + slice);
+    for (int c = c_beg + threadIdx.x; c < c_end; c += kThreads) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[i] = 0.0f;
+        for (int q = 0; q < n; ++q) {
+            const int64_t r = s_rows[q];
+            float p[8];
+            if (BF16_IN) {
+                const u32x4 v = __builtin_nontemporal_load((const u32x4 *)partials + r * nvec + c);
+                p[0] = bf16_lo(v.x); p[1] = bf16_hi(v.x); p[2] = bf16_lo(v.y); p[3] = bf16_hi(v.y);
+                p[4] = bf16_lo(v.z); p[5] = bf16_hi(v.z); p[6] = bf16_lo(v.w); p[7] = bf16_hi(v.w);
+            } else {
+                const u32x4 *src = (const u32x4 *)partials + (r * nvec + c) * 2;
+                const u32x4 a = __builtin_nontemporal_load(src), b = __builtin_nontemporal_load(src + 1);
+                p[0] = __uint_as_float(a.x); p[1] = __uint_as_float(a.y);
+                p[2] = __uint_as_float(a.z); p[3] = __uint_as_float(a.w);
+                p[4] = __uint_as_float(b.x); p[5] = __uint_as_float(b.y);
+                p[6] = __uint_as_float(b.z); p[7] = __uint_as_float(b.w);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] = acc[i] + p[i];
+        }
+        u32x4 o;
+        o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+        o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+        o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+        o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+        __builtin_nontemporal_store(o, out + t * nvec + c);
+    }
+}
+
+// Column slices so that about `target` workgroups cover `rows` rows.
+int slices_for(int64_t rows, int nvec, int align, int target)
+{
+    int want = rows >= target ? 1 : (int)((target + rows - 1) / rows);
+    int width = (nvec + want - 1) / want;
+    width = ((width + align - 1) / align) * align;
+    if (width < 4 * align && nvec > 4 * align)
+        width = 4 * align;
+    return width < nvec ? width : nvec;
+}
+
+}  // namespace
+
+hipError_t launch_relay_fanout(const Geometry &g, const epx_layout &L, const void *relay_rows,
+                               const float *relay_scales, int64_t row_bytes, int nsc,
+                               void *recv, float *recv_scales, hipStream_t stream)
+{
+    const int64_t cap = (int64_t)g.T * (g.k < g.H ? g.k : g.H);
+    const int row_vec = (int)(row_bytes / 16);
+    const int slice = slices_for(cap, row_vec, kWave, 2048);
+    const dim3 grid((unsigned)cap, (row_vec + slice - 1) / slice);
+    hipLaunchKernelGGL(relay_fanout_kernel, grid, dim3(kThreads), 0, stream,
+                       (const u32x4 *)relay_rows, relay_scales, row_vec, nsc, slice, g.k, L,
+                       (u32x4 *)recv, recv_scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_relay_partials(const Geometry &g, const epx_layout &L, const void *y,
+                                 const float *w, int32_t hidden, bool bf16_out, void *partials,
+                                 hipStream_t stream)
+{
+    const int64_t cap = (int64_t)g.T * (g.k < g.H ? g.k : g.H);
+    const int nvec = hidden / 8;
+    const int slice = slices_for(cap, nvec, kWave, 2048);
+    const dim3 grid((unsigned)cap, (nvec + slice - 1) / slice);
+    if (bf16_out)
+        hipLaunchKernelGGL(relay_partials_kernel<true>, grid, dim3(kThreads), 0, stream,
+                           (const u32x4 *)y, nvec, slice, w, g.k, L, partials);
+    else
+        hipLaunchKernelGGL(relay_partials_kernel<false>, grid, dim3(kThreads), 0, stream,
+                           (const u32x4 *)y, nvec, slice, w, g.k, L, partials);
+    return hipGetLastError();
+}
+
+hipError_t launch_relay_finish(const Geometry &g, const epx_layout &L, const void *partials,
+                               bool bf16_in, int32_t hidden, void *out, hipStream_t stream)
+{
+    const int nvec = hidden / 8;
+    const int slice = slices_for(g.T, nvec, kWave, 2048);
+    const dim3 grid(g.T, (nvec + slice - 1) / slice);
+    if (bf16_in)
+        hipLaunchKernelGGL(relay_finish_kernel<true>, grid, dim3(kThreads), 0, stream, partials,
+                           nvec, slice, g.H, L, (u32x4 *)out);
+    else
+        hipLaunchKernelGGL(relay_finish_kernel<false>, grid, dim3(kThreads), 0, stream, partials,
+                           nvec, slice, g.H, L, (u32x4 *)out);
+    return hipGetLastError();
+}
+
+}  // namespace epx

@@ -25,6 +25,7 @@ MODE_PER_EXPERT = 0
 MODE_HOST_RELAY = 1
 BF16 = 0
 FP8_E4M3 = 1
+F32 = 2
 
 STATUS = {0: "EPX_OK", 1: "EPX_ERR_ARG", 2: "EPX_ERR_INDEX", 3: "EPX_ERR_CAPACITY", 4: "EPX_ERR_DEVICE"}
 
@@ -52,10 +53,18 @@ _lib.epx_combine.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_lay
                              ctypes.c_int64, _P, ctypes.c_int32, _P, _P]
 _lib.epx_read_error.argtypes = [ctypes.POINTER(epx_layout), ctypes.POINTER(ctypes.c_int32), _P]
 _lib.epx_f32_to_e4m3.argtypes = [_P, _P, ctypes.c_int64, _P]
+_lib.epx_relay_fanout.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_layout), _P, _P,
+                                  ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int64, _P]
+_lib.epx_combine_relay_partials.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_layout), _P,
+                                            ctypes.c_int64, _P, ctypes.c_int32, ctypes.c_int32, _P,
+                                            ctypes.c_int64, _P]
+_lib.epx_combine_relay_finish.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_layout), _P,
+                                          ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P]
 _lib.epx_status_string.argtypes = [ctypes.c_int]
 _lib.epx_status_string.restype = ctypes.c_char_p
 for _f in ("epx_layout_sizes", "epx_get_layout", "epx_dispatch", "epx_combine", "epx_read_error",
-           "epx_f32_to_e4m3"):
+           "epx_f32_to_e4m3", "epx_relay_fanout", "epx_combine_relay_partials",
+           "epx_combine_relay_finish"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.epx_abi_version.restype = ctypes.c_int32
 NARRAYS = len(LAYOUT_FIELDS)
@@ -184,6 +193,58 @@ def epx_f32_to_e4m3(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:
         raise ValueError("in/out sizes differ")
     _check(_lib.epx_f32_to_e4m3(inp.data_ptr(), out.data_ptr(), inp.numel(), _stream(stream)),
            "epx_f32_to_e4m3")
+
+
+def epx_relay_fanout(problem: epx_problem, layout: Layout, relay_rows: torch.Tensor, recv: torch.Tensor,
+                     relay_scales: Optional[torch.Tensor] = None, recv_scales: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    """Relay rows -> per-expert rows (bf16 rows, or fp8 codes with scales)."""
+    fp8 = relay_rows.dtype == torch.uint8
+    _need(relay_rows, torch.uint8 if fp8 else torch.bfloat16, "relay_rows", 2)
+    _need(recv, relay_rows.dtype, "recv", 2)
+    hidden = relay_rows.shape[1]
+    if recv.shape[1] != hidden:
+        raise ValueError("recv: hidden differs from relay_rows")
+    if fp8:
+        _need(relay_scales, torch.float32, "relay_scales", 2)
+        _need(recv_scales, torch.float32, "recv_scales", 2)
+    _check(_lib.epx_relay_fanout(ctypes.byref(problem), ctypes.byref(layout.struct), relay_rows.data_ptr(),
+                                 relay_scales.data_ptr() if fp8 else None, relay_rows.shape[0], hidden,
+                                 FP8_E4M3 if fp8 else BF16, recv.data_ptr(),
+                                 recv_scales.data_ptr() if fp8 else None, recv.shape[0], _stream(stream)),
+           "epx_relay_fanout")
+
+
+def epx_combine_relay_partials(problem: epx_problem, layout: Layout, y: torch.Tensor,
+                               topk_weights: torch.Tensor, partials: torch.Tensor, stream=None) -> None:
+    """Per relay row fp32 (float32 tensor) or bf16 (bfloat16 tensor) partial sums."""
+    _need(y, torch.bfloat16, "y", 2)
+    _need(topk_weights, torch.float32, "topk_weights", 2)
+    if partials.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("partials: float32 or bfloat16")
+    _need(partials, partials.dtype, "partials", 2)
+    if partials.shape[1] != y.shape[1]:
+        raise ValueError("partials: hidden differs from y")
+    pd = F32 if partials.dtype == torch.float32 else BF16
+    _check(_lib.epx_combine_relay_partials(ctypes.byref(problem), ctypes.byref(layout.struct), y.data_ptr(),
+                                           y.shape[0], topk_weights.data_ptr(), y.shape[1], pd,
+                                           partials.data_ptr(), partials.shape[0], _stream(stream)),
+           "epx_combine_relay_partials")
+
+
+def epx_combine_relay_finish(problem: epx_problem, layout: Layout, partials: torch.Tensor,
+                             out: torch.Tensor, stream=None) -> None:
+    if partials.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("partials: float32 or bfloat16")
+    _need(partials, partials.dtype, "partials", 2)
+    _need(out, torch.bfloat16, "out", 2)
+    if tuple(out.shape) != (problem.num_tokens, partials.shape[1]):
+        raise ValueError("out: need [T, hidden]")
+    pd = F32 if partials.dtype == torch.float32 else BF16
+    _check(_lib.epx_combine_relay_finish(ctypes.byref(problem), ctypes.byref(layout.struct),
+                                         partials.data_ptr(), partials.shape[0], pd, partials.shape[1],
+                                         out.data_ptr(), _stream(stream)),
+           "epx_combine_relay_finish")
 
 
 def relay_capacity(problem: epx_problem) -> int:

@@ -12,6 +12,8 @@
  *   epx_dispatch     -- token rows -> per-expert rows (Mode 1) or one row per
  *                       destination host (Mode 2 relay), bf16 or fp8
  *   epx_combine      -- k expert outputs per token -> weighted sum, bf16
+ *   epx_relay_fanout, epx_combine_relay_partials, epx_combine_relay_finish
+ *                    -- the relay's receive side and its two-level combine
  *
  * Conventions for every call:
  *  - Every array argument is a DEVICE pointer the caller allocated; the
@@ -63,10 +65,10 @@ typedef enum {
  *             de-redundancy). */
 typedef enum { EPX_MODE_PER_EXPERT = 0, EPX_MODE_HOST_RELAY = 1 } epx_mode;
 
-/* Dispatch payload. FP8_E4M3: OCP E4M3FN codes with one float32 scale per
- * 128 channels (the BF16-to-FP8 conversion inside dispatch, digest section
- * 3.1). */
-typedef enum { EPX_BF16 = 0, EPX_FP8_E4M3 = 1 } epx_dtype;
+/* Row payloads. FP8_E4M3: OCP E4M3FN codes with one float32 scale per 128
+ * channels (the BF16-to-FP8 conversion inside dispatch, digest section 3.1).
+ * F32: float32 rows (relay partial sums only). */
+typedef enum { EPX_BF16 = 0, EPX_FP8_E4M3 = 1, EPX_F32 = 2 } epx_dtype;
 
 /* The problem of one source rank. Experts sit on ranks in contiguous
  * blocks (rank(e) = e / (num_experts/num_ranks)), ranks on hosts in
@@ -163,6 +165,44 @@ EPX_API epx_status epx_dispatch(const epx_problem *p, const epx_layout *layout, 
 EPX_API epx_status epx_combine(const epx_problem *p, const epx_layout *layout, const void *y,
                        int64_t y_rows, const float *topk_weights, int32_t hidden, void *out,
                        void *stream);
+
+/* ---- Host relay, receive side and two-level combine (digest section 3.2,
+ * Mode 2 with de-redundancy, Figure 3). Problem mode must be HOST_RELAY.
+ * C = T * min(k, H) is the relay row capacity. ---- */
+
+/* Fan-out at the same-index GPU of a host: every relay row r (token t) is
+ * copied to the per-expert rows slot[t, j] of the token's experts j on that
+ * host (fanout_expert[r, j] >= 0). dtype EPX_BF16: rows are bf16 [*, hidden];
+ * EPX_FP8_E4M3: rows are uint8 codes [*, hidden] with float32 scales
+ * [*, hidden/128] (relay_scales / recv_scales). relay_rows holds at least
+ * relay_capacity_rows >= C rows, recv at least capacity_rows >= T*k. Applied
+ * to the rows of a HOST_RELAY dispatch, recv equals what a PER_EXPERT dispatch
+ * writes. */
+EPX_API epx_status epx_relay_fanout(const epx_problem *p, const epx_layout *layout,
+                                    const void *relay_rows, const float *relay_scales,
+                                    int64_t relay_capacity_rows, int32_t hidden, int32_t dtype,
+                                    void *recv, float *recv_scales, int64_t capacity_rows,
+                                    void *stream);
+
+/* Level 1, at the relay GPU: for relay row r = (t, h),
+ * partials[r, :] = sum over j ascending with fanout_expert[r, j] >= 0 of
+ * topk_weights[t, j] * y[slot[t, j], :], accumulated as fp32 fma from +0 and
+ * stored as EPX_F32 (float32 [C, hidden]) or EPX_BF16 (rounded to nearest
+ * even, bf16 [C, hidden], the compact return form). y as in epx_combine;
+ * partial_capacity_rows >= C. */
+EPX_API epx_status epx_combine_relay_partials(const epx_problem *p, const epx_layout *layout,
+                                              const void *y, int64_t y_rows,
+                                              const float *topk_weights, int32_t hidden,
+                                              int32_t partial_dtype, void *partials,
+                                              int64_t partial_capacity_rows, void *stream);
+
+/* Level 2, at the source: out[t, :] = bf16( sum over hosts h ascending with
+ * relay_slot[t, h] >= 0 of partials[relay_slot[t, h], :] ), fp32 adds from
+ * +0, rounded to nearest even. */
+EPX_API epx_status epx_combine_relay_finish(const epx_problem *p, const epx_layout *layout,
+                                            const void *partials, int64_t partial_capacity_rows,
+                                            int32_t partial_dtype, int32_t hidden, void *out,
+                                            void *stream);
 
 /* Synchronises `stream`, then reads totals[3]: EPX_OK, or EPX_ERR_INDEX when
  * the last layout on this layout's arrays saw out-of-range expert ids (their
