@@ -23,6 +23,9 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
   relay_partials / relay_finish -- one host reduces to the flat combine bit for
                     bit; partial membership by exact power-of-two tagging;
                     float64 sum within the float32 bound.
+  plan_swaps     -- the worked example of digest Figure 2(b) (160/100 -> 130/130);
+                    optimality of every chosen swap by enumeration; pairing,
+                    threshold and conservation invariants.
   relay row order, zero-block rule, fma order: parity unpinned by the pages
                     (fixed by the readings recorded in the design notes).
 """
@@ -76,6 +79,8 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.oracle_relay_partials.restype = ctypes.c_int
     lib.oracle_relay_finish.argtypes = [i32] * 4 + [P] * 3
     lib.oracle_relay_finish.restype = ctypes.c_int
+    lib.oracle_plan_swaps.argtypes = [i32] * 3 + [P] * 2 + [i32] + [P] * 4
+    lib.oracle_plan_swaps.restype = ctypes.c_int
     for name in ("oracle_f32_to_e4m3_array", "oracle_f32_to_bf16_array", "oracle_e4m3_to_f32_array"):
         getattr(lib, name).argtypes = [P, P, ctypes.c_int64]
         getattr(lib, name).restype = None
@@ -232,6 +237,26 @@ def relay_finish(partials: np.ndarray, lay: dict, num_tokens: int, num_hosts: in
     if rc != 0:
         raise OracleError(rc, "oracle_relay_finish")
     return out
+
+
+def plan_swaps(counts: np.ndarray, num_ranks: int, num_hosts: int, tau: int,
+               slot_expert: Optional[np.ndarray] = None, lib=None) -> dict:
+    """Intra-host swap plan (see oracle_plan_swaps). Returns the placement
+    after the swaps, loads before/after and the per-pair records [.., 7]."""
+    lib = lib or load()
+    c = np.ascontiguousarray(counts, dtype=np.int32)
+    E, R, H = c.size, num_ranks, num_hosts
+    se = np.arange(E, dtype=np.int32) if slot_expert is None else np.ascontiguousarray(slot_expert, np.int32)
+    out = np.zeros(E, np.int32)
+    lb = np.zeros(R, np.int32)
+    la = np.zeros(R, np.int32)
+    npair = (R // H) // 2
+    sw = np.full((H * max(npair, 0), 7), -1, np.int32)
+    rc = lib.oracle_plan_swaps(E, R, H, _p(c), _p(se), tau, _p(out), _p(lb), _p(la),
+                               _p(sw if sw.size else np.zeros(7, np.int32)))
+    if rc != 0:
+        raise OracleError(rc, "oracle_plan_swaps")
+    return {"slot_expert": out, "load_before": lb, "load_after": la, "swaps": sw}
 
 
 def f32_to_e4m3(a: np.ndarray, lib=None) -> np.ndarray:

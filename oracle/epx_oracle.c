@@ -561,3 +561,100 @@ int oracle_relay_finish(int32_t T, int32_t H, int32_t hidden, int32_t bf16_in,
         }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* Per-step intra-host expert swap planner                             */
+/* ------------------------------------------------------------------ */
+/*
+ * Digest section 3.1 and Figure 2(b): every step the load of each GPU is the
+ * sum of its experts' token counts; inside each host the heaviest GPU pairs
+ * with the lightest, the second heaviest with the second lightest, and so
+ * on; each pair takes the one expert swap that most lowers its maximum, and
+ * only when the maximum falls by at least tau tokens.
+ *
+ * Placement: slot_expert[r * epr + i] is the expert in slot i of rank r.
+ * Ties: ranks are ordered by load descending, then rank index ascending;
+ * among equally good swaps the one with the smaller slot of the heavier rank,
+ * then the smaller slot of the lighter rank, wins. A swap must lower the
+ * pair's maximum strictly and by at least tau to be applied.
+ *
+ * Outputs: slot_expert_out (the placement after the applied swaps), loads
+ * per rank before and after, and per pair (host-major, pair index within the
+ * host) 7 ints: heavy rank, its expert, light rank, its expert, old maximum,
+ * new maximum, applied (0/1); -1 entries when a host has no such pair.
+ */
+int oracle_plan_swaps(int32_t E, int32_t R, int32_t H, const int32_t *count,
+                      const int32_t *slot_expert_in, int32_t tau, int32_t *slot_expert_out,
+                      int32_t *load_before, int32_t *load_after, int32_t *swaps)
+{
+    if (E < 1 || R < 1 || H < 1 || E % R != 0 || R % H != 0 || tau < 0)
+        return ORC_ERR_ARG;
+    const int32_t epr = E / R, rph = R / H, npair = rph / 2;
+    for (int32_t i = 0; i < E; ++i) {
+        if (slot_expert_in[i] < 0 || slot_expert_in[i] >= E)
+            return ORC_ERR_INDEX;
+        slot_expert_out[i] = slot_expert_in[i];
+    }
+    for (int32_t r = 0; r < R; ++r) {
+        int64_t load = 0;
+        for (int32_t i = 0; i < epr; ++i)
+            load += count[slot_expert_in[r * epr + i]];
+        load_before[r] = (int32_t)load;
+    }
+    int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)(rph > 0 ? rph : 1));
+    if (!order)
+        return ORC_ERR_ARG;
+    for (int32_t h = 0; h < H; ++h) {
+        /* ranks of host h by load descending, rank ascending (insertion sort) */
+        for (int32_t i = 0; i < rph; ++i) {
+            int32_t r = h * rph + i, pos = i;
+            while (pos > 0) {
+                int32_t q = order[pos - 1];
+                if (load_before[q] > load_before[r] || (load_before[q] == load_before[r] && q < r))
+                    break;
+                order[pos] = q;
+                pos -= 1;
+            }
+            order[pos] = r;
+        }
+        for (int32_t p = 0; p < npair; ++p) {
+            int32_t A = order[p], B = order[rph - 1 - p];
+            int32_t LA = load_before[A], LB = load_before[B];
+            int32_t old_max = LA > LB ? LA : LB;
+            int32_t best = -1, best_a = 0, best_b = 0;
+            for (int32_t a = 0; a < epr; ++a)
+                for (int32_t b = 0; b < epr; ++b) {
+                    int32_t ca = count[slot_expert_in[A * epr + a]];
+                    int32_t cb = count[slot_expert_in[B * epr + b]];
+                    int32_t na = LA - ca + cb, nb = LB - cb + ca;
+                    int32_t m = na > nb ? na : nb;
+                    if (best < 0 || m < best) {   /* strict: the first (a, b) keeps ties */
+                        best = m;
+                        best_a = a;
+                        best_b = b;
+                    }
+                }
+            int32_t applied = (old_max - best > 0) && (old_max - best >= tau);
+            int32_t *rec = swaps + ((int64_t)h * npair + p) * 7;
+            rec[0] = A;
+            rec[1] = slot_expert_in[A * epr + best_a];
+            rec[2] = B;
+            rec[3] = slot_expert_in[B * epr + best_b];
+            rec[4] = old_max;
+            rec[5] = best;
+            rec[6] = applied;
+            if (applied) {
+                slot_expert_out[A * epr + best_a] = slot_expert_in[B * epr + best_b];
+                slot_expert_out[B * epr + best_b] = slot_expert_in[A * epr + best_a];
+            }
+        }
+    }
+    free(order);
+    for (int32_t r = 0; r < R; ++r) {
+        int64_t load = 0;
+        for (int32_t i = 0; i < epr; ++i)
+            load += count[slot_expert_out[r * epr + i]];
+        load_after[r] = (int32_t)load;
+    }
+    return ORC_OK;
+}

@@ -19,6 +19,7 @@ import oracle
 from tests import test_oracle_layout as TL
 from tests import test_oracle_numerics as TN
 from tests import test_oracle_relay as TRL
+from tests import test_oracle_swaps as TSW
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "epx_oracle.c")
 
@@ -93,6 +94,18 @@ MUTANTS = [
     ("finish reads the first host only",
      "                int32_t r = relay_slot[(int64_t)t * H + h];\n                if (r < 0)\n                    continue;\n                float p",
      "                int32_t r = relay_slot[(int64_t)t * H];\n                if (r < 0)\n                    continue;\n                float p"),
+    ("swap pairs heaviest with the second lightest",
+     "            int32_t A = order[p], B = order[rph - 1 - p];",
+     "            int32_t A = order[p], B = order[rph - 2 - p < p ? rph - 1 - p : rph - 2 - p];"),
+    ("swap ties keep the last candidate",
+     "                    if (best < 0 || m < best) {   /* strict: the first (a, b) keeps ties */",
+     "                    if (best < 0 || m <= best) {"),
+    ("swap ignores the threshold",
+     "            int32_t applied = (old_max - best > 0) && (old_max - best >= tau);",
+     "            int32_t applied = (old_max - best > 0);"),
+    ("swap sorts lightest first",
+     "                if (load_before[q] > load_before[r] || (load_before[q] == load_before[r] && q < r))",
+     "                if (load_before[q] < load_before[r] || (load_before[q] == load_before[r] && q < r))"),
     ("combine subtracts",
      "                acc = fmaf(w[(int64_t)t * k + j], v, acc);",
      "                acc = fmaf(-w[(int64_t)t * k + j], v, acc);"),
@@ -128,6 +141,10 @@ def _pins():
     calls.append(lambda: TRL.test_fanout_of_relay_dispatch_is_per_expert_dispatch(TRL.SHAPES[1]))
     calls.append(lambda: TRL.test_one_host_two_level_is_flat(8, 256, 32))
     calls.append(lambda: TRL.test_two_level_within_bounds_of_float64(TRL.SHAPES[1]))
+    calls.append(TSW.test_figure_example)
+    for case in TSW.CASES:
+        calls.append(lambda c=case: TSW.test_swaps_optimal_and_consistent(c, 5))
+    calls.append(TSW.test_degenerate_cases)
     return calls
 
 
