@@ -193,6 +193,9 @@ def main(argv=None) -> int:
                          "per-host partials and the source-side finish (instead of the flat combine)")
     ap.add_argument("--partials", choices=["f32", "bf16"], default="f32",
                     help="wire form of the relay partials (with --relay-receive)")
+    ap.add_argument("--swap-planner", type=int, default=None, metavar="TAU",
+                    help="also run the per-step intra-host swap planner on the layout's expert counts "
+                         "(threshold TAU tokens) between layout and dispatch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -257,12 +260,31 @@ def main(argv=None) -> int:
         part = torch.empty((cap, hidden), dtype=torch.float32 if args.partials == "f32" else torch.bfloat16,
                            device=dev)
 
+    planner = args.swap_planner is not None
+    if planner:
+        # the placement ping-pongs between two buffers: each step plans from
+        # the previous step's placement
+        E, R, H = w.num_experts, w.num_ranks, w.num_hosts
+        places = [torch.arange(E, dtype=torch.int32, device=dev), torch.empty(E, dtype=torch.int32, device=dev)]
+        plan_out = {"slot_expert": None, "load_before": torch.empty(R, dtype=torch.int32, device=dev),
+                    "load_after": torch.empty(R, dtype=torch.int32, device=dev),
+                    "swaps": torch.empty((H * ((R // H) // 2), 7), dtype=torch.int32, device=dev),
+                    "host_bad": torch.empty(H, dtype=torch.int32, device=dev)}
+        n_plans = [0]
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         epx.epx_get_layout(p, idx, L, stream)
         if ev is not None:
             ev[1].record(stream)
+        if planner:
+            i = n_plans[0] % 2
+            plan_out["slot_expert"] = places[1 - i]
+            epx.epx_plan_swaps(E, R, H, L["expert_count"], places[i], args.swap_planner, plan_out, stream)
+            n_plans[0] += 1
+        if ev is not None:
+            ev[6].record(stream)
         epx.epx_dispatch(p, L, x, out_dtype, recv, scales, stream)
         if ev is not None:
             ev[2].record(stream)
@@ -296,7 +318,7 @@ def main(argv=None) -> int:
     totals = L["totals"].cpu().numpy()
     rows = int(totals[1] if relay else totals[0])
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -305,7 +327,8 @@ def main(argv=None) -> int:
     wall = time.perf_counter() - t0
 
     lay_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    dis_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    plan_ms = np.array([e[1].elapsed_time(e[6]) for e in evs])
+    dis_ms = np.array([e[6].elapsed_time(e[2]) for e in evs])
     if receive:
         fan_ms = np.array([e[2].elapsed_time(e[4]) for e in evs])
         par_ms = np.array([e[4].elapsed_time(e[5]) for e in evs])
@@ -328,6 +351,11 @@ def main(argv=None) -> int:
         "layout": {"us": float(lay_ms.mean() * 1e3), "bytes": nbytes["layout"]},
         "dispatch": {"us": float(dis_ms.mean() * 1e3), "bytes": nbytes["dispatch"]},
     }
+    if planner:
+        # counts and placement in, placement, loads, pair records and flags out
+        npair = H * ((R // H) // 2)
+        per_kernel["swap_planner"] = {"us": float(plan_ms.mean() * 1e3),
+                                      "bytes": 4 * (3 * E + 2 * R + 7 * npair + H)}
     if receive:
         per_kernel["relay_fanout"] = {"us": float(fan_ms.mean() * 1e3), "bytes": nbytes["relay_fanout"]}
         per_kernel["relay_partials"] = {"us": float(par_ms.mean() * 1e3), "bytes": nbytes["relay_partials"]}
@@ -337,7 +365,7 @@ def main(argv=None) -> int:
     for v in per_kernel.values():
         v["GBs"] = v["bytes"] / (v["us"] * 1e-6) / 1e9
         v["frac_peak"] = v["GBs"] / PEAK_HBM_GBS
-    dom = max((n for n in per_kernel if n != "layout"), key=lambda n: per_kernel[n]["us"])
+    dom = max((n for n in per_kernel if n not in ("layout", "swap_planner")), key=lambda n: per_kernel[n]["us"])
     kname = {"dispatch": "dispatch_fp8_kernel" if fp8 else "dispatch_bf16_kernel",
              "combine": "combine_kernel", "relay_fanout": "relay_fanout_kernel",
              "relay_partials": "relay_partials_kernel", "relay_finish": "relay_finish_kernel"}[dom]
@@ -366,7 +394,8 @@ def main(argv=None) -> int:
         "config": {"workload": args.workload, "tokens": T, "hidden": hidden, "experts": w.num_experts,
                    "topk": k, "ranks": w.num_ranks, "hosts": w.num_hosts, "routing": w.routing,
                    "mode": mode + ("+receive" if receive else ""), "payload": dtype,
-                   **({"partials": args.partials} if receive else {})},
+                   **({"partials": args.partials} if receive else {}),
+                   **({"swap_tau": args.swap_planner} if planner else {})},
         "us_per_layer": round(us_layer, 2),
         "pct_of_peak_layer": round(100 * layer_bytes / (us_layer * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
         "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}

@@ -297,6 +297,30 @@ epx_status epx_read_error(const epx_layout *layout, int32_t *bad_count, void *st
     return totals[3] == 0 ? EPX_OK : EPX_ERR_INDEX;
 }
 
+epx_status epx_plan_swaps(int32_t num_experts, int32_t num_ranks, int32_t num_hosts,
+                          const int32_t *expert_count, const int32_t *slot_expert_in,
+                          int32_t tau, int32_t *slot_expert_out, int32_t *rank_load_before,
+                          int32_t *rank_load_after, int32_t *swaps, int32_t *host_bad,
+                          void *stream)
+{
+    const int32_t E = num_experts, R = num_ranks, H = num_hosts;
+    if (E < 1 || E > epx::kMaxExperts || R < 1 || H < 1 || H > epx::kMaxHosts || E % R != 0 ||
+        R % H != 0 || R / H > epx::kMaxRanksPerHost || tau < 0)
+        return EPX_ERR_ARG;
+    const void *need[] = {expert_count, slot_expert_in, slot_expert_out, rank_load_before,
+                          rank_load_after, host_bad};
+    for (const void *q : need)
+        if (!q || !aligned(q, 4))
+            return EPX_ERR_ARG;
+    if (R / H >= 2 && (!swaps || !aligned(swaps, 4)))
+        return EPX_ERR_ARG;
+    if (slot_expert_out == slot_expert_in)
+        return EPX_ERR_ARG;
+    return from_hip(epx::launch_plan_swaps(E, R, H, expert_count, slot_expert_in, tau,
+                                           slot_expert_out, rank_load_before, rank_load_after,
+                                           swaps, host_bad, (hipStream_t)stream));
+}
+
 epx_status epx_f32_to_e4m3(const float *in, uint8_t *out, int64_t n, void *stream)
 {
     if (n < 0 || (n > 0 && (!in || !out || !aligned(in, 4))))

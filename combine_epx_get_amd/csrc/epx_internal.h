@@ -69,5 +69,9 @@ hipError_t launch_relay_partials(const Geometry &g, const epx_layout &L, const v
                                  hipStream_t stream);
 hipError_t launch_relay_finish(const Geometry &g, const epx_layout &L, const void *partials,
                                bool bf16_in, int32_t hidden, void *out, hipStream_t stream);
+hipError_t launch_plan_swaps(int E, int R, int H, const int32_t *count, const int32_t *slot_in,
+                             int tau, int32_t *slot_out, int32_t *load_before,
+                             int32_t *load_after, int32_t *swaps, int32_t *host_bad,
+                             hipStream_t stream);
 
 }  // namespace epx

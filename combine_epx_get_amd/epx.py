@@ -60,11 +60,13 @@ _lib.epx_combine_relay_partials.argtypes = [ctypes.POINTER(epx_problem), ctypes.
                                             ctypes.c_int64, _P]
 _lib.epx_combine_relay_finish.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_layout), _P,
                                           ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P]
+_lib.epx_plan_swaps.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32,
+                                _P, _P, _P, _P, _P, _P]
 _lib.epx_status_string.argtypes = [ctypes.c_int]
 _lib.epx_status_string.restype = ctypes.c_char_p
 for _f in ("epx_layout_sizes", "epx_get_layout", "epx_dispatch", "epx_combine", "epx_read_error",
            "epx_f32_to_e4m3", "epx_relay_fanout", "epx_combine_relay_partials",
-           "epx_combine_relay_finish"):
+           "epx_combine_relay_finish", "epx_plan_swaps"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.epx_abi_version.restype = ctypes.c_int32
 NARRAYS = len(LAYOUT_FIELDS)
@@ -245,6 +247,33 @@ def epx_combine_relay_finish(problem: epx_problem, layout: Layout, partials: tor
                                          partials.data_ptr(), partials.shape[0], pd, partials.shape[1],
                                          out.data_ptr(), _stream(stream)),
            "epx_combine_relay_finish")
+
+
+def epx_plan_swaps(num_experts: int, num_ranks: int, num_hosts: int, expert_count: torch.Tensor,
+                   slot_expert: torch.Tensor, tau: int, out: Optional[dict] = None, stream=None) -> dict:
+    """Per-step intra-host expert swaps. Returns (and fills, if given) the
+    int32 tensors slot_expert [E], load_before [R], load_after [R],
+    swaps [H * (R/H)//2, 7] and host_bad [H]."""
+    E, R, H = num_experts, num_ranks, num_hosts
+    _need(expert_count, torch.int32, "expert_count", 1)
+    _need(slot_expert, torch.int32, "slot_expert", 1)
+    if expert_count.numel() < E or slot_expert.numel() != E:
+        raise ValueError("expert_count needs >= E entries, slot_expert exactly E")
+    npair = H * ((R // H) // 2) if H > 0 and R % H == 0 else 0
+    shapes = {"slot_expert": (E,), "load_before": (R,), "load_after": (R,), "swaps": (npair, 7),
+              "host_bad": (H,)}
+    if out is None:
+        out = {n: torch.empty(sh, dtype=torch.int32, device=slot_expert.device) for n, sh in shapes.items()}
+    for n, sh in shapes.items():
+        _need(out[n], torch.int32, n)
+        if tuple(out[n].shape) != sh:
+            raise ValueError(f"{n}: need shape {sh}")
+    _check(_lib.epx_plan_swaps(E, R, H, expert_count.data_ptr(), slot_expert.data_ptr(), tau,
+                               out["slot_expert"].data_ptr(), out["load_before"].data_ptr(),
+                               out["load_after"].data_ptr(), out["swaps"].data_ptr() if npair else None,
+                               out["host_bad"].data_ptr(), _stream(stream)),
+           "epx_plan_swaps")
+    return out
 
 
 def relay_capacity(problem: epx_problem) -> int:

@@ -14,6 +14,7 @@
  *   epx_combine      -- k expert outputs per token -> weighted sum, bf16
  *   epx_relay_fanout, epx_combine_relay_partials, epx_combine_relay_finish
  *                    -- the relay's receive side and its two-level combine
+ *   epx_plan_swaps   -- per-step expert swaps between GPUs of one host
  *
  * Conventions for every call:
  *  - Every array argument is a DEVICE pointer the caller allocated; the
@@ -203,6 +204,34 @@ EPX_API epx_status epx_combine_relay_finish(const epx_problem *p, const epx_layo
                                             const void *partials, int64_t partial_capacity_rows,
                                             int32_t partial_dtype, int32_t hidden, void *out,
                                             void *stream);
+
+/* ---- Per-step intra-host expert swaps (digest section 3.1, Figure 2(b)).
+ * Experts sit in slots: slot_expert[r * (E/R) + i] is the expert in slot i of
+ * rank r (E/R slots per rank, ranks h*(R/H) .. (h+1)*(R/H)-1 on host h). The
+ * load of a rank is the sum of expert_count over its slots (expert_count may
+ * be a layout's EPX_L_EXPERT_COUNT). In every host the ranks are ordered by
+ * load descending, then rank index; the i-th heaviest pairs with the i-th
+ * lightest (i < (R/H)/2; an odd middle rank stays unpaired). Each pair takes
+ * the single expert exchange that gives the smallest new pair maximum (ties:
+ * smaller slot of the heavier rank, then smaller slot of the lighter rank)
+ * and applies it only if the maximum falls by at least max(tau, 1) tokens;
+ * tau is the swap cost in token units (weight-move time over per-token time).
+ *
+ * Device arrays: expert_count int32 [E] (non-negative, total < 2^31);
+ * slot_expert_in / slot_expert_out int32 [E] (distinct buffers);
+ * rank_load_before / rank_load_after int32 [R];
+ * swaps int32 [H * ((R/H)/2) * 7], per pair host-major: heavy rank, its
+ * expert, light rank, its expert, old maximum, new maximum, applied (0/1)
+ * (may be NULL when R/H < 2); host_bad int32 [H].
+ * A host whose slots hold an id outside [0, E) is not planned: its slots are
+ * copied unchanged, its loads and records are -1 (applied 0) and host_bad[h]
+ * is the number of such ids (0 for a planned host).
+ * Limits: E <= 2048, H <= 64, R/H <= 32, tau >= 0; else EPX_ERR_ARG. */
+EPX_API epx_status epx_plan_swaps(int32_t num_experts, int32_t num_ranks, int32_t num_hosts,
+                                  const int32_t *expert_count, const int32_t *slot_expert_in,
+                                  int32_t tau, int32_t *slot_expert_out,
+                                  int32_t *rank_load_before, int32_t *rank_load_after,
+                                  int32_t *swaps, int32_t *host_bad, void *stream);
 
 /* Synchronises `stream`, then reads totals[3]: EPX_OK, or EPX_ERR_INDEX when
  * the last layout on this layout's arrays saw out-of-range expert ids (their

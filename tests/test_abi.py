@@ -136,6 +136,33 @@ def test_host_checks_of_the_calls(epx):
     assert lib.epx_read_error(None, None, None) == 1
 
 
+@pytest.mark.parametrize("args", [
+    # E, R, H, tau, and which pointer (by position) is bad
+    (16, 3, 1, 0, None),        # E % R
+    (16, 4, 3, 0, None),        # R % H
+    (4096, 4, 1, 0, None),      # E above the limit
+    (128, 64, 1, 0, None),      # 64 ranks on one host
+    (128, 128, 128, 0, None),   # H above the limit
+    (16, 4, 2, -1, None),       # negative tau
+    (16, 4, 2, 0, 0),           # no expert_count
+    (16, 4, 2, 0, 1),           # no slot_expert_in
+    (16, 4, 2, 0, 6),           # no swaps with two ranks per host
+    (16, 4, 2, 0, "alias"),     # output aliases input
+    (16, 4, 2, 0, "misaligned"),
+])
+def test_plan_swaps_host_checks(epx, args):
+    E, R, H, tau, bad = args
+    ptrs = [0x300000 + 0x1000 * i for i in range(7)]   # count, in, out, before, after, swaps, bad
+    if isinstance(bad, int):
+        ptrs[bad if bad < 5 else 5] = None
+    elif bad == "alias":
+        ptrs[2] = ptrs[1]
+    elif bad == "misaligned":
+        ptrs[3] += 2
+    c, i, o, lb, la, sw, hb = ptrs
+    assert epx._lib.epx_plan_swaps(E, R, H, c, i, tau, o, lb, la, sw, hb, None) == 1
+
+
 def test_binding_rejects_wrong_tensors(epx):
     import torch
     p = epx.make_problem(4, 2, 16, 4, 2)
