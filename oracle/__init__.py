@@ -23,6 +23,12 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
   relay_partials / relay_finish -- one host reduces to the flat combine bit for
                     bit; partial membership by exact power-of-two tagging;
                     float64 sum within the float32 bound.
+  layout_grouped -- m = 1 equals the plain layout; brute-force sort by
+                    (group, expert, token, j) on small inputs; block offsets.
+  group_slots    -- the union over groups is the full slot array, groups disjoint.
+  combine_grouped -- m = 1 equals the plain combine bit for bit; an order
+                    case whose float32 result differs between j order and
+                    group order (exact expected values); float64 bound.
   plan_swaps     -- the worked example of digest Figure 2(b) (160/100 -> 130/130);
                     optimality of every chosen swap by enumeration; pairing,
                     threshold and conservation invariants.
@@ -79,6 +85,12 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.oracle_relay_partials.restype = ctypes.c_int
     lib.oracle_relay_finish.argtypes = [i32] * 4 + [P] * 3
     lib.oracle_relay_finish.restype = ctypes.c_int
+    lib.oracle_layout_grouped.argtypes = [i32] * 5 + [P] * 7
+    lib.oracle_layout_grouped.restype = ctypes.c_int
+    lib.oracle_group_slots.argtypes = [i32] * 6 + [P] * 3
+    lib.oracle_group_slots.restype = ctypes.c_int
+    lib.oracle_combine_grouped.argtypes = [i32] * 6 + [P] * 5
+    lib.oracle_combine_grouped.restype = ctypes.c_int
     lib.oracle_plan_swaps.argtypes = [i32] * 3 + [P] * 2 + [i32] + [P] * 4
     lib.oracle_plan_swaps.restype = ctypes.c_int
     for name in ("oracle_f32_to_e4m3_array", "oracle_f32_to_bf16_array", "oracle_e4m3_to_f32_array"):
@@ -181,6 +193,66 @@ def combine(y_bits: np.ndarray, lay: dict, topk_weights: np.ndarray, lib=None) -
     rc = lib.oracle_combine(T, k, hidden, _p(lay["slot"]), _p(w), _p(y), _p(out))
     if rc != 0:
         raise OracleError(rc, "oracle_combine")
+    return out
+
+
+def layout_grouped(topk_idx: np.ndarray, num_experts: int, num_ranks: int, num_groups: int,
+                   lib=None) -> dict:
+    """Per-expert layout with rows ordered by (expert group, expert, token, j)."""
+    lib = lib or load()
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, k = idx.shape
+    E, R, m = num_experts, num_ranks, num_groups
+    out = {"expert_count": np.zeros(E, np.int32), "expert_offset": np.zeros(E + 1, np.int32),
+           "group_offset": np.zeros(m * R + 1, np.int32), "slot": np.zeros(T * k, np.int32),
+           "row_token": np.zeros(T * k, np.int32), "totals": np.zeros(4, np.int32)}
+    rc = lib.oracle_layout_grouped(T, k, E, R, m, _p(idx), *[_p(out[n]) for n in (
+        "expert_count", "expert_offset", "group_offset", "slot", "row_token", "totals")])
+    if rc != 0:
+        raise OracleError(rc, "oracle_layout_grouped")
+    return out
+
+
+def group_slots(topk_idx: np.ndarray, lay: dict, num_experts: int, num_ranks: int, num_groups: int,
+                group: int, lib=None) -> np.ndarray:
+    """slot[t, j] where expert idx[t, j] is in the group, -1 elsewhere."""
+    lib = lib or load()
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, k = idx.shape
+    out = np.zeros(T * k, np.int32)
+    rc = lib.oracle_group_slots(T, k, num_experts, num_ranks, num_groups, group, _p(idx),
+                                _p(lay["slot"]), _p(out))
+    if rc != 0:
+        raise OracleError(rc, "oracle_group_slots")
+    return out
+
+
+def dispatch_group(x_bits: np.ndarray, lay: dict, topk_idx: np.ndarray, num_experts: int,
+                   num_ranks: int, num_groups: int, group: int, fp8: bool = False, lib=None):
+    """Rows [T*k, ...] of one group's dispatch (other groups' rows zero): the
+    per-expert dispatch over that group's destinations only."""
+    k = topk_idx.shape[1]
+    sub = {"slot": group_slots(topk_idx, lay, num_experts, num_ranks, num_groups, group, lib),
+           "totals": lay["totals"]}
+    if fp8:
+        return dispatch_fp8(x_bits, sub, k, 1, False, lib=lib)
+    return dispatch_bf16(x_bits, sub, k, 1, False, lib=lib)
+
+
+def combine_grouped(y_bits: np.ndarray, lay: dict, topk_idx: np.ndarray, topk_weights: np.ndarray,
+                    num_experts: int, num_ranks: int, num_groups: int, lib=None) -> np.ndarray:
+    """out [T, h] bf16 bits after the m group combines (float32 carried across groups)."""
+    lib = lib or load()
+    y = np.ascontiguousarray(y_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(topk_weights, dtype=np.float32)
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, k = w.shape
+    hidden = y.shape[1]
+    out = np.zeros((T, hidden), np.uint16)
+    rc = lib.oracle_combine_grouped(T, k, num_experts, num_ranks, num_groups, hidden, _p(idx),
+                                    _p(lay["slot"]), _p(w), _p(y), _p(out))
+    if rc != 0:
+        raise OracleError(rc, "oracle_combine_grouped")
     return out
 
 

@@ -29,6 +29,10 @@
  *    weights (digest section 3.2, "Combine sums", and section 3.4, combine
  *    buffers sized batch x k), accumulated in float32 with fmaf in ascending
  *    j from +0, rounded once to bf16 (nearest, ties to even).
+ *  - Relay receive side and two-level combine (digest section 3.2, Mode 2,
+ *    Figure 3), expert groups for per-expert overlap (section 3.3, Figure 4)
+ *    and the per-step intra-host swap planner (section 3.1, Figure 2(b)):
+ *    see each section below.
  *
  * Readings where the pages are silent (all listed with reasons in the design
  * notes of the repository): experts map to ranks in contiguous blocks and
@@ -557,6 +561,136 @@ int oracle_relay_finish(int32_t T, int32_t H, int32_t hidden, int32_t bf16_in,
                                   : ((const float *)partials)[(int64_t)r * hidden + c];
                 acc = acc + p;
             }
+            out[(int64_t)t * hidden + c] = oracle_f32_to_bf16(acc);
+        }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Expert groups (per-expert overlap)                                  */
+/* ------------------------------------------------------------------ */
+/*
+ * Digest section 3.3 and Figure 4: instead of splitting the batch, the
+ * experts are split into m groups (2 or 4) that are dispatched, computed and
+ * combined one after another, the whole batch in every group, so each expert
+ * weight is loaded once. Every GPU must have work in every group for the
+ * overlap to exist, so group g holds, on every rank, the local experts i
+ * (i = e mod epr) with i / (epr / m) == g.
+ *
+ * Rows: per-expert rows ordered by (group, expert id, token, j). Group g's
+ * rows are then one contiguous range, and inside it each rank's rows are
+ * contiguous: group_offset[g * R + r] is the first row of group g on rank r,
+ * group_offset[m * R] the total. With m == 1 this is the plain layout.
+ *
+ * Combine: each group adds its experts' weighted outputs to the float32 sum
+ * the earlier groups left, in ascending j inside the group; the result is
+ * rounded to bf16 once, after the last group: acc = +0, then for g = 0..m-1,
+ * for j ascending with group(idx[t, j]) == g, acc = fmaf(w[t, j], y, acc).
+ */
+
+static int32_t group_of(int32_t e, int32_t epr, int32_t m)
+{
+    return (e % epr) / (epr / m);
+}
+
+int oracle_layout_grouped(int32_t T, int32_t k, int32_t E, int32_t R, int32_t m,
+                          const int32_t *idx, int32_t *expert_count, int32_t *expert_offset,
+                          int32_t *group_offset, int32_t *slot, int32_t *row_token,
+                          int32_t *totals)
+{
+    if (T < 0 || k < 1 || E < 1 || R < 1 || m < 1 || E % R != 0 || (E / R) % m != 0)
+        return ORC_ERR_ARG;
+    const int32_t epr = E / R, epg = epr / m;
+    const int64_t P = (int64_t)T * k;
+    int64_t bad = 0;
+    for (int64_t p = 0; p < P; ++p)
+        if (idx[p] < 0 || idx[p] >= E)
+            bad += 1;
+    totals[0] = 0;
+    totals[1] = 0;
+    totals[2] = 0;
+    totals[3] = (int32_t)bad;
+    if (bad)
+        return ORC_ERR_INDEX;
+
+    for (int32_t e = 0; e < E; ++e)
+        expert_count[e] = 0;
+    for (int64_t p = 0; p < P; ++p)
+        expert_count[idx[p]] += 1;
+
+    /* experts in (group, expert id) order; prefix sums in that order */
+    int32_t run = 0;
+    for (int32_t g = 0; g < m; ++g)
+        for (int32_t r = 0; r < R; ++r) {
+            group_offset[g * R + r] = run;
+            for (int32_t i = g * epg; i < (g + 1) * epg; ++i) {
+                int32_t e = r * epr + i;
+                expert_offset[e] = run;
+                run += expert_count[e];
+            }
+        }
+    group_offset[m * R] = run;
+    expert_offset[E] = run;
+
+    /* rows of each expert fill up from its offset in (t, j) order */
+    int32_t *next = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    if (!next)
+        return ORC_ERR_ARG;
+    for (int32_t e = 0; e < E; ++e)
+        next[e] = expert_offset[e];
+    for (int32_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t e = idx[(int64_t)t * k + j];
+            slot[(int64_t)t * k + j] = next[e];
+            row_token[next[e]] = t;
+            next[e] += 1;
+        }
+    free(next);
+
+    int32_t mx = 0;
+    for (int32_t e = 0; e < E; ++e)
+        if (expert_count[e] > mx)
+            mx = expert_count[e];
+    totals[0] = (int32_t)P;
+    totals[2] = mx;
+    return ORC_OK;
+}
+
+/* The destinations of group g's dispatch: slot[t, j] where expert idx[t, j]
+ * is in group g, -1 elsewhere (a per-expert dispatch over these rows copies
+ * exactly group g's rows). */
+int oracle_group_slots(int32_t T, int32_t k, int32_t E, int32_t R, int32_t m, int32_t g,
+                       const int32_t *idx, const int32_t *slot, int32_t *slot_g)
+{
+    if (T < 0 || k < 1 || E < 1 || R < 1 || m < 1 || E % R != 0 || (E / R) % m != 0 || g < 0 ||
+        g >= m)
+        return ORC_ERR_ARG;
+    const int32_t epr = E / R;
+    for (int64_t p = 0; p < (int64_t)T * k; ++p)
+        slot_g[p] = group_of(idx[p], epr, m) == g ? slot[p] : -1;
+    return ORC_OK;
+}
+
+int oracle_combine_grouped(int32_t T, int32_t k, int32_t E, int32_t R, int32_t m,
+                           int32_t hidden, const int32_t *idx, const int32_t *slot,
+                           const float *w, const uint16_t *y, uint16_t *out)
+{
+    if (T < 0 || k < 1 || E < 1 || R < 1 || m < 1 || E % R != 0 || (E / R) % m != 0 ||
+        hidden < 1)
+        return ORC_ERR_ARG;
+    const int32_t epr = E / R;
+    for (int32_t t = 0; t < T; ++t)
+        for (int32_t c = 0; c < hidden; ++c) {
+            float acc = 0.0f;
+            for (int32_t g = 0; g < m; ++g)
+                for (int32_t j = 0; j < k; ++j) {
+                    if (group_of(idx[(int64_t)t * k + j], epr, m) != g)
+                        continue;
+                    int32_t row = slot[(int64_t)t * k + j];
+                    float wt = w[(int64_t)t * k + j];
+                    float v = oracle_bf16_to_f32(y[(int64_t)row * hidden + c]);
+                    acc = fmaf(wt, v, acc);
+                }
             out[(int64_t)t * hidden + c] = oracle_f32_to_bf16(acc);
         }
     return ORC_OK;

@@ -16,6 +16,7 @@ import tempfile
 import pytest
 
 import oracle
+from tests import test_oracle_groups as TG
 from tests import test_oracle_layout as TL
 from tests import test_oracle_numerics as TN
 from tests import test_oracle_relay as TRL
@@ -106,6 +107,27 @@ MUTANTS = [
     ("swap sorts lightest first",
      "                if (load_before[q] > load_before[r] || (load_before[q] == load_before[r] && q < r))",
      "                if (load_before[q] < load_before[r] || (load_before[q] == load_before[r] && q < r))"),
+    ("groups interleave the local experts",
+     "    return (e % epr) / (epr / m);",
+     "    return (e % epr) % m;"),
+    ("grouped rows j-major",
+     "    for (int32_t t = 0; t < T; ++t)\n        for (int32_t j = 0; j < k; ++j) {\n            int32_t e = idx[(int64_t)t * k + j];\n            slot[(int64_t)t * k + j] = next[e];",
+     "    for (int32_t j = 0; j < k; ++j)\n        for (int32_t t = 0; t < T; ++t) {\n            int32_t e = idx[(int64_t)t * k + j];\n            slot[(int64_t)t * k + j] = next[e];"),
+    ("grouped offsets rank-major",
+     "    for (int32_t g = 0; g < m; ++g)\n        for (int32_t r = 0; r < R; ++r) {\n            group_offset[g * R + r] = run;",
+     "    for (int32_t r = 0; r < R; ++r)\n        for (int32_t g = 0; g < m; ++g) {\n            group_offset[g * R + r] = run;"),
+    ("grouped combine takes the groups last to first",
+     "            for (int32_t g = 0; g < m; ++g)\n                for (int32_t j = 0; j < k; ++j) {\n                    if (group_of",
+     "            for (int32_t g = m - 1; g >= 0; --g)\n                for (int32_t j = 0; j < k; ++j) {\n                    if (group_of"),
+    ("grouped combine in plain j order",
+     "                    if (group_of(idx[(int64_t)t * k + j], epr, m) != g)\n                        continue;",
+     "                    if (g != 0)\n                        continue;"),
+    ("grouped combine subtracts",
+     "                    acc = fmaf(wt, v, acc);",
+     "                    acc = fmaf(-wt, v, acc);"),
+    ("group slots keep later groups",
+     "        slot_g[p] = group_of(idx[p], epr, m) == g ? slot[p] : -1;",
+     "        slot_g[p] = group_of(idx[p], epr, m) >= g ? slot[p] : -1;"),
     ("combine subtracts",
      "                acc = fmaf(w[(int64_t)t * k + j], v, acc);",
      "                acc = fmaf(-w[(int64_t)t * k + j], v, acc);"),
@@ -141,6 +163,11 @@ def _pins():
     calls.append(lambda: TRL.test_fanout_of_relay_dispatch_is_per_expert_dispatch(TRL.SHAPES[1]))
     calls.append(lambda: TRL.test_one_host_two_level_is_flat(8, 256, 32))
     calls.append(lambda: TRL.test_two_level_within_bounds_of_float64(TRL.SHAPES[1]))
+    for shape in TG.SHAPES:
+        calls.append(lambda sh=shape: TG.test_grouped_layout_brute_force(sh, False))
+        calls.append(lambda sh=shape: TG.test_group_dispatches_cover_every_row_once(sh))
+    calls.append(TG.test_combine_order_cases)
+    calls.append(lambda: TG.test_one_group_is_the_plain_layout_and_combine((30, 4, 16, 4, 1)))
     calls.append(TSW.test_figure_example)
     for case in TSW.CASES:
         calls.append(lambda c=case: TSW.test_swaps_optimal_and_consistent(c, 5))
