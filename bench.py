@@ -55,9 +55,39 @@ def algorithmic_bytes(T, k, H, hidden, rows, relay, fp8):
     return {"dispatch": dispatch, "combine": combine, "layout": layout}
 
 
+def group_bytes(idx, E, R, m, hidden, fp8):
+    """Algorithmic bytes of each expert group's dispatch and combine.
+
+    Pairs of group g: expert local index (e mod E/R) // (E/R/m) == g.
+    dispatch g: read x for the tokens with a pair in g, the whole slot array
+                (T*k*4: the group's pairs must be found), write the group's
+                rows.
+    combine g:  read the group's rows (bf16), slots (T*k*4) and the group's
+                weights; read the float32 carry for tokens that had pairs in
+                an earlier group, write it for tokens with pairs in a later
+                group, write bf16 out for tokens whose last group is g.
+    """
+    T, k = idx.shape
+    epr = E // R
+    grp = (idx % epr) // (epr // m)
+    row_bytes = hidden + (hidden // 128) * 4 if fp8 else hidden * 2
+    out = {}
+    for g in range(m):
+        pairs = int((grp == g).sum())
+        in_g = (grp == g).any(axis=1)
+        prior = int((in_g & (grp < g).any(axis=1)).sum())
+        later = int((in_g & (grp > g).any(axis=1)).sum())
+        final = int(in_g.sum()) - later
+        out[f"dispatch_g{g}"] = int(in_g.sum()) * hidden * 2 + T * k * 4 + pairs * row_bytes
+        out[f"combine_g{g}"] = (pairs * hidden * 2 + T * k * 4 + pairs * 4 + prior * hidden * 4
+                                + later * hidden * 4 + final * hidden * 2)
+    return out
+
+
 KERNEL_SOURCE = {"dispatch_bf16_kernel": "epx_dispatch.hip", "dispatch_fp8_kernel": "epx_dispatch.hip",
                  "combine_kernel": "epx_combine.hip", "relay_fanout_kernel": "epx_relay.hip",
-                 "relay_partials_kernel": "epx_relay.hip", "relay_finish_kernel": "epx_relay.hip"}
+                 "relay_partials_kernel": "epx_relay.hip", "relay_finish_kernel": "epx_relay.hip",
+                 "combine_group_kernel": "epx_combine.hip", "plan_swaps_kernel": "epx_balance.hip"}
 
 
 def relay_receive_bytes(T, k, H, hidden, rows, fp8, f32_partials):
@@ -106,7 +136,7 @@ def load_counter_traffic(kernel: str, tag: str):
 KERNEL_NAMES = ("dispatch_bf16_kernel", "dispatch_fp8_kernel", "combine_kernel",
                 "relay_fanout_kernel", "relay_partials_kernel", "relay_finish_kernel",
                 "layout_small_kernel", "layout_count_kernel", "layout_scan_kernel",
-                "layout_assign_kernel")
+                "layout_assign_kernel", "combine_group_kernel", "plan_swaps_kernel")
 
 
 def ingest_counters(fetch_csv: str, write_csv: str, tag: str, command: str) -> list:
@@ -196,6 +226,9 @@ def main(argv=None) -> int:
     ap.add_argument("--swap-planner", type=int, default=None, metavar="TAU",
                     help="also run the per-step intra-host swap planner on the layout's expert counts "
                          "(threshold TAU tokens) between layout and dispatch")
+    ap.add_argument("--groups", type=int, default=1, metavar="M",
+                    help="expert groups (per-expert overlap): step = grouped layout, M group "
+                         "dispatches, M group combines (per-expert mode)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -207,6 +240,8 @@ def main(argv=None) -> int:
         w0 = args.workload
         from combine_epx_get_amd import workloads as W0
         tag0 = f"{w0}_{args.mode or W0.WORKLOADS[w0].modes[0]}_{args.dtype or W0.WORKLOADS[w0].dtypes[0]}"
+        if args.groups > 1:
+            tag0 += f"_g{args.groups}"
         for pth in ingest_counters(*args.ingest_counters, tag0, args.ingest_command):
             print(pth)
         return 0
@@ -231,8 +266,12 @@ def main(argv=None) -> int:
 
     d = W.make_inputs(w)
     T, k, hidden = d["T"], w.topk, w.hidden
+    m = args.groups
+    if m > 1 and relay:
+        print("--groups needs per-expert mode", file=sys.stderr)
+        return 2
     p = epx.make_problem(T, k, w.num_experts, w.num_ranks, w.num_hosts, w.my_rank,
-                         epx.MODE_HOST_RELAY if relay else epx.MODE_PER_EXPERT)
+                         epx.MODE_HOST_RELAY if relay else epx.MODE_PER_EXPERT, m)
     L = epx.Layout(p, dev)
     idx = torch.from_numpy(d["topk_idx"]).to(dev)
     x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
@@ -260,6 +299,8 @@ def main(argv=None) -> int:
         part = torch.empty((cap, hidden), dtype=torch.float32 if args.partials == "f32" else torch.bfloat16,
                            device=dev)
 
+    if m > 1:
+        carry = torch.empty((T, hidden), dtype=torch.float32, device=dev)
     planner = args.swap_planner is not None
     if planner:
         # the placement ping-pongs between two buffers: each step plans from
@@ -273,33 +314,42 @@ def main(argv=None) -> int:
         n_plans = [0]
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+        def rec(i):
+            if ev is not None:
+                ev[i].record(stream)
+
+        rec(0)
         epx.epx_get_layout(p, idx, L, stream)
-        if ev is not None:
-            ev[1].record(stream)
+        rec(1)
         if planner:
             i = n_plans[0] % 2
             plan_out["slot_expert"] = places[1 - i]
             epx.epx_plan_swaps(E, R, H, L["expert_count"], places[i], args.swap_planner, plan_out, stream)
             n_plans[0] += 1
-        if ev is not None:
-            ev[6].record(stream)
+        rec(6)
+        if m > 1:
+            # per-expert overlap order without the expert GEMMs: every group's
+            # dispatch, then every group's combine (events 7.. per launch)
+            for g in range(m):
+                epx.epx_dispatch_group(p, L, g, x, out_dtype, recv, scales, stream)
+                rec(7 + g)
+            rec(2)
+            for g in range(m):
+                epx.epx_combine_group(p, L, g, y, wts, carry, out, stream)
+                rec(7 + m + g)
+            rec(3)
+            return
         epx.epx_dispatch(p, L, x, out_dtype, recv, scales, stream)
-        if ev is not None:
-            ev[2].record(stream)
+        rec(2)
         if receive:
             epx.epx_relay_fanout(p, L, recv, fan, scales, fan_sc, stream)
-            if ev is not None:
-                ev[4].record(stream)
+            rec(4)
             epx.epx_combine_relay_partials(p, L, y, wts, part, stream)
-            if ev is not None:
-                ev[5].record(stream)
+            rec(5)
             epx.epx_combine_relay_finish(p, L, part, out, stream)
         else:
             epx.epx_combine(p, L, y, wts, out, stream)
-        if ev is not None:
-            ev[3].record(stream)
+        rec(3)
 
     if args.copy_calibration:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give
@@ -318,7 +368,7 @@ def main(argv=None) -> int:
     totals = L["totals"].cpu().numpy()
     rows = int(totals[1] if relay else totals[0])
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7 + 2 * m)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -343,14 +393,24 @@ def main(argv=None) -> int:
     if receive:
         nbytes.update(relay_receive_bytes(T, k, w.num_hosts, hidden, rows, fp8, args.partials == "f32"))
         del nbytes["combine"]
+    if m > 1:
+        nbytes = {"layout": nbytes["layout"],
+                  **group_bytes(d["topk_idx"], w.num_experts, w.num_ranks, m, hidden, fp8)}
     layer_bytes = sum(nbytes.values())
     us_layer = float(step_ms.mean() * 1e3)
     value = layer_bytes / (ms_per_step * 1e-3) / 1e9
 
-    per_kernel = {
-        "layout": {"us": float(lay_ms.mean() * 1e3), "bytes": nbytes["layout"]},
-        "dispatch": {"us": float(dis_ms.mean() * 1e3), "bytes": nbytes["dispatch"]},
-    }
+    per_kernel = {"layout": {"us": float(lay_ms.mean() * 1e3), "bytes": nbytes["layout"]}}
+    if m == 1:
+        per_kernel["dispatch"] = {"us": float(dis_ms.mean() * 1e3), "bytes": nbytes["dispatch"]}
+    if m > 1:
+        for g in range(m):
+            d0 = 6 if g == 0 else 7 + g - 1
+            c0 = 2 if g == 0 else 7 + m + g - 1
+            per_kernel[f"dispatch_g{g}"] = {"us": float(np.mean([e[d0].elapsed_time(e[7 + g]) for e in evs]) * 1e3),
+                                            "bytes": nbytes[f"dispatch_g{g}"]}
+            per_kernel[f"combine_g{g}"] = {"us": float(np.mean([e[c0].elapsed_time(e[7 + m + g]) for e in evs]) * 1e3),
+                                           "bytes": nbytes[f"combine_g{g}"]}
     if planner:
         # counts and placement in, placement, loads, pair records and flags out
         npair = H * ((R // H) // 2)
@@ -360,7 +420,7 @@ def main(argv=None) -> int:
         per_kernel["relay_fanout"] = {"us": float(fan_ms.mean() * 1e3), "bytes": nbytes["relay_fanout"]}
         per_kernel["relay_partials"] = {"us": float(par_ms.mean() * 1e3), "bytes": nbytes["relay_partials"]}
         per_kernel["relay_finish"] = {"us": float(fin_ms.mean() * 1e3), "bytes": nbytes["relay_finish"]}
-    else:
+    elif m == 1:
         per_kernel["combine"] = {"us": float(com_ms.mean() * 1e3), "bytes": nbytes["combine"]}
     for v in per_kernel.values():
         v["GBs"] = v["bytes"] / (v["us"] * 1e-6) / 1e9
@@ -368,8 +428,11 @@ def main(argv=None) -> int:
     dom = max((n for n in per_kernel if n not in ("layout", "swap_planner")), key=lambda n: per_kernel[n]["us"])
     kname = {"dispatch": "dispatch_fp8_kernel" if fp8 else "dispatch_bf16_kernel",
              "combine": "combine_kernel", "relay_fanout": "relay_fanout_kernel",
-             "relay_partials": "relay_partials_kernel", "relay_finish": "relay_finish_kernel"}[dom]
-    traffic = load_counter_traffic(kname, f"{args.workload}_{mode}_{dtype}")
+             "relay_partials": "relay_partials_kernel", "relay_finish": "relay_finish_kernel",
+             "dispatch_g": "dispatch_fp8_kernel" if fp8 else "dispatch_bf16_kernel",
+             "combine_g": "combine_group_kernel"}[dom.rstrip("0123456789")]
+    tag = f"{args.workload}_{mode}_{dtype}" + (f"_g{m}" if m > 1 else "")
+    traffic = load_counter_traffic(kname, tag)
     roofline = {"bound": "hbm", "kernel": kname,
                 "achieved": round(per_kernel[dom]["GBs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(per_kernel[dom]["frac_peak"], 4), "traffic": traffic,
@@ -395,7 +458,8 @@ def main(argv=None) -> int:
                    "topk": k, "ranks": w.num_ranks, "hosts": w.num_hosts, "routing": w.routing,
                    "mode": mode + ("+receive" if receive else ""), "payload": dtype,
                    **({"partials": args.partials} if receive else {}),
-                   **({"swap_tau": args.swap_planner} if planner else {})},
+                   **({"swap_tau": args.swap_planner} if planner else {}),
+                   **({"expert_groups": m} if m > 1 else {})},
         "us_per_layer": round(us_layer, 2),
         "pct_of_peak_layer": round(100 * layer_bytes / (us_layer * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
         "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}

@@ -28,6 +28,9 @@ epx_status make_geometry(const epx_problem *p, Geometry *g)
         return EPX_ERR_ARG;
     if ((int64_t)T * k >= ((int64_t)1 << 31))
         return EPX_ERR_ARG;
+    const int32_t m = p->num_groups == 0 ? 1 : p->num_groups;
+    if (m < 1 || (E / R) % m != 0 || (m > 1 && p->mode != EPX_MODE_PER_EXPERT))
+        return EPX_ERR_ARG;
     g->T = T;
     g->k = k;
     g->E = E;
@@ -47,6 +50,8 @@ epx_status make_geometry(const epx_problem *p, Geometry *g)
         ++nbits;
     g->nbits = nbits;
     g->relay = p->mode == EPX_MODE_HOST_RELAY;
+    g->m = m;
+    g->epg = g->epr / m;
     return EPX_OK;
 }
 
@@ -70,6 +75,7 @@ void sizes_of(const Geometry &g, int64_t s[EPX_LAYOUT_NARRAYS])
     s[EPX_L_FANOUT_RANK_MASK] = cap;
     s[EPX_L_RELAY_DST_RANK] = g.H;
     s[EPX_L_TOTALS] = 4;
+    s[EPX_L_GROUP_OFFSET] = (int64_t)g.m * g.R + 1;
     s[EPX_L_WORKSPACE] = (int64_t)(g.Gs + 1) * (g.E + g.R + g.H + 1);
 }
 
@@ -81,7 +87,7 @@ epx_status check_layout(const Geometry &g, const epx_layout *L)
         return EPX_ERR_ARG;
     const void *need[] = {L->expert_count, L->expert_offset, L->rank_rows, L->rank_tokens,
                           L->rank_offset, L->host_tokens, L->host_offset, L->slot,
-                          L->row_token, L->relay_dst_rank, L->totals};
+                          L->row_token, L->relay_dst_rank, L->totals, L->group_offset};
     for (const void *q : need)
         if (!q || !aligned(q, 4))
             return EPX_ERR_ARG;
@@ -97,6 +103,70 @@ epx_status check_layout(const Geometry &g, const epx_layout *L)
 }
 
 epx_status from_hip(hipError_t e) { return e == hipSuccess ? EPX_OK : EPX_ERR_DEVICE; }
+
+// group < 0: the plain call; else one group's rows (group < m).
+epx_status dispatch_impl(const epx_problem *p, const epx_layout *layout, int group, const void *x,
+                         int32_t hidden, int32_t out_dtype, void *recv, float *recv_scales,
+                         int64_t capacity_rows, void *stream)
+{
+    Geometry g;
+    epx_status st = make_geometry(p, &g);
+    if (st != EPX_OK)
+        return st;
+    if ((st = check_layout(g, layout)) != EPX_OK)
+        return st;
+    if (group >= g.m)
+        return EPX_ERR_ARG;
+    if (g.m == 1)
+        group = -1;   // one group is every row (relay rows included)
+    if (out_dtype != EPX_BF16 && out_dtype != EPX_FP8_E4M3)
+        return EPX_ERR_ARG;
+    if (hidden < 8 || hidden % 8 != 0 || (out_dtype == EPX_FP8_E4M3 && hidden % epx::kFp8Block != 0))
+        return EPX_ERR_ARG;
+    const int64_t need = g.relay ? relay_capacity(g) : (int64_t)g.T * g.k;
+    if (capacity_rows < need)
+        return EPX_ERR_CAPACITY;
+    if (g.T == 0)
+        return EPX_OK;   // nothing to move; the activation pointers are not used
+    if (!x || !recv || !aligned(x, 16) || !aligned(recv, 16))
+        return EPX_ERR_ARG;
+    if (out_dtype == EPX_FP8_E4M3 && (!recv_scales || !aligned(recv_scales, 4)))
+        return EPX_ERR_ARG;
+    const hipStream_t s = (hipStream_t)stream;
+    if (out_dtype == EPX_BF16)
+        return from_hip(epx::launch_dispatch_bf16(g, *layout, x, hidden, recv, group, s));
+    return from_hip(epx::launch_dispatch_fp8(g, *layout, x, hidden, recv, recv_scales, group, s));
+}
+
+epx_status combine_impl(const epx_problem *p, const epx_layout *layout, int group, const void *y,
+                        int64_t y_rows, const float *topk_weights, int32_t hidden, float *carry,
+                        void *out, void *stream)
+{
+    Geometry g;
+    epx_status st = make_geometry(p, &g);
+    if (st != EPX_OK)
+        return st;
+    if ((st = check_layout(g, layout)) != EPX_OK)
+        return st;
+    if (group >= g.m)
+        return EPX_ERR_ARG;
+    if (hidden < 8 || hidden % 8 != 0)
+        return EPX_ERR_ARG;
+    if (y_rows < (int64_t)g.T * g.k)
+        return EPX_ERR_CAPACITY;
+    if (g.T == 0)
+        return EPX_OK;
+    if (!y || !out || !topk_weights || !aligned(y, 16) || !aligned(out, 16) ||
+        !aligned(topk_weights, 4))
+        return EPX_ERR_ARG;
+    const hipStream_t s = (hipStream_t)stream;
+    if (group < 0 || g.m == 1)
+        return from_hip(epx::launch_combine(g, *layout, y, topk_weights, hidden, out, s));
+    if (!carry || !aligned(carry, 16))
+        return EPX_ERR_ARG;
+    return from_hip(
+        epx::launch_combine_group(g, *layout, group, y, topk_weights, hidden, carry, out, s));
+}
 
 }  // namespace
 
@@ -151,52 +221,34 @@ epx_status epx_dispatch(const epx_problem *p, const epx_layout *layout, const vo
                         int32_t hidden, int32_t out_dtype, void *recv, float *recv_scales,
                         int64_t capacity_rows, void *stream)
 {
-    Geometry g;
-    epx_status st = make_geometry(p, &g);
-    if (st != EPX_OK)
-        return st;
-    if ((st = check_layout(g, layout)) != EPX_OK)
-        return st;
-    if (out_dtype != EPX_BF16 && out_dtype != EPX_FP8_E4M3)
+    return dispatch_impl(p, layout, -1, x, hidden, out_dtype, recv, recv_scales, capacity_rows,
+                         stream);
+}
+
+epx_status epx_dispatch_group(const epx_problem *p, const epx_layout *layout, int32_t group,
+                              const void *x, int32_t hidden, int32_t out_dtype, void *recv,
+                              float *recv_scales, int64_t capacity_rows, void *stream)
+{
+    if (group < 0)
         return EPX_ERR_ARG;
-    if (hidden < 8 || hidden % 8 != 0 || (out_dtype == EPX_FP8_E4M3 && hidden % epx::kFp8Block != 0))
-        return EPX_ERR_ARG;
-    const int64_t need = g.relay ? relay_capacity(g) : (int64_t)g.T * g.k;
-    if (capacity_rows < need)
-        return EPX_ERR_CAPACITY;
-    if (g.T == 0)
-        return EPX_OK;   // nothing to move; the activation pointers are not used
-    if (!x || !recv || !aligned(x, 16) || !aligned(recv, 16))
-        return EPX_ERR_ARG;
-    if (out_dtype == EPX_FP8_E4M3 && (!recv_scales || !aligned(recv_scales, 4)))
-        return EPX_ERR_ARG;
-    const hipStream_t s = (hipStream_t)stream;
-    if (out_dtype == EPX_BF16)
-        return from_hip(epx::launch_dispatch_bf16(g, *layout, x, hidden, recv, s));
-    return from_hip(epx::launch_dispatch_fp8(g, *layout, x, hidden, recv, recv_scales, s));
+    return dispatch_impl(p, layout, group, x, hidden, out_dtype, recv, recv_scales, capacity_rows,
+                         stream);
 }
 
 epx_status epx_combine(const epx_problem *p, const epx_layout *layout, const void *y,
                        int64_t y_rows, const float *topk_weights, int32_t hidden, void *out,
                        void *stream)
 {
-    Geometry g;
-    epx_status st = make_geometry(p, &g);
-    if (st != EPX_OK)
-        return st;
-    if ((st = check_layout(g, layout)) != EPX_OK)
-        return st;
-    if (hidden < 8 || hidden % 8 != 0)
+    return combine_impl(p, layout, -1, y, y_rows, topk_weights, hidden, nullptr, out, stream);
+}
+
+epx_status epx_combine_group(const epx_problem *p, const epx_layout *layout, int32_t group,
+                             const void *y, int64_t y_rows, const float *topk_weights,
+                             int32_t hidden, float *carry, void *out, void *stream)
+{
+    if (group < 0)
         return EPX_ERR_ARG;
-    if (y_rows < (int64_t)g.T * g.k)
-        return EPX_ERR_CAPACITY;
-    if (g.T == 0)
-        return EPX_OK;
-    if (!y || !out || !topk_weights || !aligned(y, 16) || !aligned(out, 16) ||
-        !aligned(topk_weights, 4))
-        return EPX_ERR_ARG;
-    return from_hip(
-        epx::launch_combine(g, *layout, y, topk_weights, hidden, out, (hipStream_t)stream));
+    return combine_impl(p, layout, group, y, y_rows, topk_weights, hidden, carry, out, stream);
 }
 
 epx_status epx_relay_fanout(const epx_problem *p, const epx_layout *layout,

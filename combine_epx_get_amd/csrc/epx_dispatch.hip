@@ -18,7 +18,8 @@
 //
 // The fp8 variant is the BF16-to-FP8 conversion that dispatch performs
 // (digest section 3.1): per token and 128-channel block, scale = amax/448 and
-// code = E4M3(x / scale). The workgroup quantises its slice once into LDS (a
+// code = E4M3(x / scale), the float32 quotient correctly rounded, then
+// rounded to nearest even in E4M3. The workgroup quantises its slice once into LDS (a
 // 16-lane group owns one 128-channel block: 8 bf16 per lane, block maximum by
 // lane shuffles), then the waves stream the codes and scales from LDS to the
 // destination rows.
@@ -31,13 +32,29 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kBurst = 4;              // 16-byte chunks per lane per burst
 constexpr int kMaxSliceVec = 4096;     // fp8 slice bound: LDS holds slice*8 code bytes
+constexpr int kPre = 4;                // fp8: 16-byte chunks loaded per thread before converting
+
+// Destination rows outside [*lo_p, *hi_p) are skipped (one expert group's
+// rows); lo_p == nullptr keeps every row.
+__device__ __forceinline__ void row_range(const int32_t *lo_p, const int32_t *hi_p, int &lo, int &hi)
+{
+    lo = 0;
+    hi = 0x7FFFFFFF;
+    if (lo_p) {
+        lo = *lo_p;
+        hi = *hi_p;
+    }
+}
 
 __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     const u32x4 *__restrict__ x, int nvec, int slice, const int32_t *__restrict__ dest, int D,
-    u32x4 *__restrict__ recv, const int32_t *__restrict__ totals)
+    u32x4 *__restrict__ recv, const int32_t *__restrict__ totals, const int32_t *lo_p,
+    const int32_t *hi_p)
 {
     if (totals[3] != 0)
         return;   // the layout saw out-of-range expert ids
+    int lo, hi;
+    row_range(lo_p, hi_p, lo, hi);
     const int64_t t = blockIdx.x;
     const int c_beg = blockIdx.y * slice;
     const int c_end = min(nvec, c_beg + slice);
@@ -45,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     const u32x4 *xr = x + t * nvec;
     for (int d = wave; d < D; d += kWaves) {
         const int64_t r = dest[t * D + d];
-        if (r < 0)
+        if (r < lo || r >= hi)
             continue;
         u32x4 *dst = recv + r * nvec;
         for (int c0 = c_beg + lane; c0 < c_end; c0 += kWave * kBurst) {
@@ -69,34 +86,68 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// float32 -> OCP E4M3FN, round to nearest even, finite values beyond +-448
-// saturate to +-448, NaN -> NaN. Normal range: round the 23-bit mantissa to 3
-// bits on the integer pattern and rebias the exponent (127 -> 7); below 2^-6
-// the codes are the integers rint(|v| * 2^9) (2^-9 steps; 8 is 2^-6 itself).
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v)
+// float32 pair -> two OCP E4M3FN codes (a in the low byte) by the packed
+// hardware conversion, which rounds to nearest even. Finite values beyond
+// +-448 are clamped first so that they saturate to +-448 (the conversion on
+// its own turns them into NaN); NaN stays a NaN code. Checked on every
+// float32 pattern against the integer definition (round the 23-bit mantissa
+// to 3 bits, rebias; below 2^-6 the codes are rint(|v| * 2^9)): identical for
+// every non-NaN input.
+__device__ __forceinline__ float clamp448(float v)
 {
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u)
-        return sign | 0x7Fu;
-    if (a >= 0x43E00000u)           // >= 448.0f
-        return sign | 0x7Eu;
-    if (a < 0x3C800000u)            // < 2^-6
-        return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    return sign | ((r >> 20) - (120u << 3));
+    return fabsf(v) > 448.0f ? __builtin_copysignf(448.0f, v) : v;
 }
 
-__device__ __forceinline__ uint32_t quantize4(float a, float b, float c, float d, float s, bool zero)
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b)
 {
-    if (zero) {   // all-zero block: scale 0, codes keep the sign of each zero
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false) & 0xFFFFu;
+}
+
+// x / s, correctly rounded, for a block scale s >= 2^-100 and |x| <= 448 s:
+// the refinement of the IEEE division expansion (reciprocal y refined once
+// per scale, two fma corrections per quotient) without its range scaling,
+// which these operands never need; the sign is restored for zero x. Over
+// every bf16 pair (x, amax) with |x| <= amax and s = amax / 448 >= 2^-100 it
+// gives the same E4M3 code as the IEEE quotient (its last bit can differ only
+// for quotients far below the smallest code).
+__device__ __forceinline__ float div_by_scale(float x, float s, float y)
+{
+    const float q0 = x * y;
+    const float r1 = __builtin_fmaf(-s, q0, x);
+    const float q1 = __builtin_fmaf(r1, y, q0);
+    const float r2 = __builtin_fmaf(-s, q1, x);
+    return __builtin_copysignf(__builtin_fmaf(r2, y, q1), x);
+}
+
+__device__ __forceinline__ float refined_reciprocal(float s)
+{
+    const float y0 = __builtin_amdgcn_rcpf(s);
+    return __builtin_fmaf(__builtin_fmaf(-s, y0, 1.0f), y0, y0);
+}
+
+// Four values of one block -> four codes (a in the low byte). zero: the
+// block is all zeros (scale 0), codes keep the sign of each zero.
+__device__ __forceinline__ uint32_t quantize4(float a, float b, float c, float d, float s, float y,
+                                              bool zero)
+{
+    if (zero) {
         return ((__float_as_uint(a) >> 24) & 0x80u) | (((__float_as_uint(b) >> 24) & 0x80u) << 8) |
                (((__float_as_uint(c) >> 24) & 0x80u) << 16) |
                (((__float_as_uint(d) >> 24) & 0x80u) << 24);
     }
-    return f32_to_e4m3(a / s) | (f32_to_e4m3(b / s) << 8) | (f32_to_e4m3(c / s) << 16) |
-           (f32_to_e4m3(d / s) << 24);
+    float qa, qb, qc, qd;
+    if (s >= 0x1p-100f) {
+        qa = div_by_scale(a, s, y);
+        qb = div_by_scale(b, s, y);
+        qc = div_by_scale(c, s, y);
+        qd = div_by_scale(d, s, y);
+    } else {   // tiny blocks: the full IEEE division
+        qa = a / s;
+        qb = b / s;
+        qc = c / s;
+        qd = d / s;
+    }
+    return e4m3_pair(qa, qb) | (e4m3_pair(qc, qd) << 16);
 }
 
 // Slice [c_beg, c_end) of token t, in 16-byte bf16 chunks (c_beg, c_end and
@@ -104,36 +155,67 @@ __device__ __forceinline__ uint32_t quantize4(float a, float b, float c, float d
 // (8 bytes per chunk) then one scale per 128-channel block.
 __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const u32x4 *__restrict__ x, int nvec, int slice, const int32_t *__restrict__ dest, int D,
-    uint8_t *__restrict__ recv, float *__restrict__ scales, const int32_t *__restrict__ totals)
+    uint8_t *__restrict__ recv, float *__restrict__ scales, const int32_t *__restrict__ totals,
+    const int32_t *lo_p, const int32_t *hi_p)
 {
     extern __shared__ u32x4 s_codes[];   // slice/2 vectors of 16 codes
     if (totals[3] != 0)
         return;
     const int64_t t = blockIdx.x;
+    int lo, hi;
+    row_range(lo_p, hi_p, lo, hi);
+    if (lo_p) {
+        // no row of this group: skip the quantisation (every wave reads all
+        // D <= 64 destinations, so the whole workgroup agrees)
+        bool any = false;
+        for (int d = threadIdx.x % kWave; d < D; d += kWave) {
+            const int r = dest[t * D + d];
+            any = any || (r >= lo && r < hi);
+        }
+        if (!__any(any))
+            return;
+    }
     const int c_beg = blockIdx.y * slice;
     const int c_end = min(nvec, c_beg + slice);
     const int n = c_end - c_beg;                       // chunks in this slice
     float *s_scale = (float *)(s_codes + (slice >> 1));
     const u32x4 *xr = x + t * nvec;
 
-    // quantise the slice once: 16 lanes per 128-channel block
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-        const u32x4 v = xr[c_beg + i];
-        const float f0 = bf16_lo(v.x), f1 = bf16_hi(v.x), f2 = bf16_lo(v.y), f3 = bf16_hi(v.y);
-        const float f4 = bf16_lo(v.z), f5 = bf16_hi(v.z), f6 = bf16_lo(v.w), f7 = bf16_hi(v.w);
-        float m = fmaxf(fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))),
-                        fmaxf(fmaxf(fabsf(f4), fabsf(f5)), fmaxf(fabsf(f6), fabsf(f7))));
+    // quantise the slice once: 16 lanes per 128-channel block. Each thread
+    // issues the loads of up to kPre chunks before converting any (n and
+    // kThreads are multiples of 16, so a 16-lane block group is either all in
+    // range or all out).
+    for (int base = 0; base < n; base += kThreads * kPre) {
+        u32x4 xv[kPre];
 #pragma unroll
-        for (int dd = 8; dd > 0; dd >>= 1)
-            m = fmaxf(m, __shfl_xor(m, dd, 16));
-        const float s = m / 448.0f;
-        const bool zero = (m == 0.0f);
-        u32x2 q;
-        q.x = quantize4(f0, f1, f2, f3, s, zero);
-        q.y = quantize4(f4, f5, f6, f7, s, zero);
-        ((u32x2 *)s_codes)[i] = q;
-        if ((i & 15) == 0)
-            s_scale[i >> 4] = s;
+        for (int p = 0; p < kPre; ++p) {
+            const int i = base + p * kThreads + threadIdx.x;
+            if (i < n)
+                xv[p] = xr[c_beg + i];
+        }
+#pragma unroll
+        for (int p = 0; p < kPre; ++p) {
+            const int i = base + p * kThreads + threadIdx.x;
+            if (i >= n)
+                break;   // uniform over each 16-lane group, and later p are out too
+            const u32x4 v = xv[p];
+            const float f0 = bf16_lo(v.x), f1 = bf16_hi(v.x), f2 = bf16_lo(v.y), f3 = bf16_hi(v.y);
+            const float f4 = bf16_lo(v.z), f5 = bf16_hi(v.z), f6 = bf16_lo(v.w), f7 = bf16_hi(v.w);
+            float m = fmaxf(fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))),
+                            fmaxf(fmaxf(fabsf(f4), fabsf(f5)), fmaxf(fabsf(f6), fabsf(f7))));
+#pragma unroll
+            for (int dd = 8; dd > 0; dd >>= 1)
+                m = fmaxf(m, __shfl_xor(m, dd, 16));
+            const float s = m / 448.0f;
+            const bool zero = (m == 0.0f);
+            const float y = refined_reciprocal(s);
+            u32x2 q;
+            q.x = quantize4(f0, f1, f2, f3, s, y, zero);
+            q.y = quantize4(f4, f5, f6, f7, s, y, zero);
+            ((u32x2 *)s_codes)[i] = q;
+            if ((i & 15) == 0)
+                s_scale[i >> 4] = s;
+        }
     }
     __syncthreads();
 
@@ -145,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const int row_blk = nvec >> 4;         // scales per row
     for (int d = wave; d < D; d += kWaves) {
         const int64_t r = dest[t * D + d];
-        if (r < 0)
+        if (r < lo || r >= hi)
             continue;
         u32x4 *dst = (u32x4 *)(recv) + r * row_vec + (c_beg >> 1);
         for (int c0 = lane; c0 < nq; c0 += kWave * kBurst) {
@@ -173,7 +255,7 @@ __global__ void f32_to_e4m3_kernel(const float *__restrict__ in, uint8_t *__rest
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-        out[i] = (uint8_t)f32_to_e4m3(in[i]);
+        out[i] = (uint8_t)(e4m3_pair(in[i], 0.0f) & 0xFFu);
 }
 
 // Column slices per token, each a whole number of `align` chunks: at least
@@ -193,21 +275,27 @@ int slice_width(int T, int nvec, int align, int max_width, int target)
 }  // namespace
 
 hipError_t launch_dispatch_bf16(const Geometry &g, const epx_layout &L, const void *x,
-                                int32_t hidden, void *recv, hipStream_t stream)
+                                int32_t hidden, void *recv, int group, hipStream_t stream)
 {
+    const int32_t *lo_p = group < 0 ? nullptr : L.group_offset + group * g.R;
+    const int32_t *hi_p = group < 0 ? nullptr : L.group_offset + (group + 1) * g.R;
     const int32_t *dest = g.relay ? L.relay_slot : L.slot;
     const int D = g.relay ? g.H : g.k;
     const int nvec = hidden / 8;
     const int slice = slice_width(g.T, nvec, kWave, 1 << 30, 2048);
     const dim3 grid(g.T, (nvec + slice - 1) / slice);
     hipLaunchKernelGGL(dispatch_bf16_kernel, grid, dim3(kThreads), 0, stream, (const u32x4 *)x,
-                       nvec, slice, dest, D, (u32x4 *)recv, (const int32_t *)L.totals);
+                       nvec, slice, dest, D, (u32x4 *)recv, (const int32_t *)L.totals, lo_p,
+                       hi_p);
     return hipGetLastError();
 }
 
 hipError_t launch_dispatch_fp8(const Geometry &g, const epx_layout &L, const void *x,
-                               int32_t hidden, void *recv, float *scales, hipStream_t stream)
+                               int32_t hidden, void *recv, float *scales, int group,
+                               hipStream_t stream)
 {
+    const int32_t *lo_p = group < 0 ? nullptr : L.group_offset + group * g.R;
+    const int32_t *hi_p = group < 0 ? nullptr : L.group_offset + (group + 1) * g.R;
     const int32_t *dest = g.relay ? L.relay_slot : L.slot;
     const int D = g.relay ? g.H : g.k;
     const int nvec = hidden / 8;          // multiple of 16 (hidden % 128 == 0)
@@ -215,11 +303,14 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const epx_layout &L, const voi
     // smaller workgroups to overlap the two: about 2048 * D per batch
     // (measured on MI355X: 2 slices for 4 relay rows per token at T = 4096,
     // 4 slices for 8 per-expert rows).
-    const int slice = slice_width(g.T, nvec, 16, kMaxSliceVec, 2048 * D);
+    // One group's dispatch writes about k/m rows per token.
+    const int rows_per_token = group < 0 ? D : (D + g.m - 1) / g.m;
+    const int slice = slice_width(g.T, nvec, 16, kMaxSliceVec, 2048 * rows_per_token);
     const dim3 grid(g.T, (nvec + slice - 1) / slice);
     const size_t lds = (size_t)slice * 8 + (size_t)(slice / 16) * sizeof(float);
     hipLaunchKernelGGL(dispatch_fp8_kernel, grid, dim3(kThreads), lds, stream, (const u32x4 *)x,
-                       nvec, slice, dest, D, (uint8_t *)recv, scales, (const int32_t *)L.totals);
+                       nvec, slice, dest, D, (uint8_t *)recv, scales, (const int32_t *)L.totals,
+                       lo_p, hi_p);
     return hipGetLastError();
 }
 

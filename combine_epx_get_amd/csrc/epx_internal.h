@@ -44,6 +44,8 @@ struct Geometry {
     int32_t Gs;      // workspace column stride: G rounded up to 4 (16-byte columns)
     int32_t nbits;   // bits that distinguish expert ids (ceil(log2 E))
     int32_t relay;   // HOST_RELAY mode
+    int32_t m;       // expert groups (1: none)
+    int32_t epg;     // experts per rank in one group: epr / m
     FastDiv div_epr, div_rph, div_k;
 };
 
@@ -54,12 +56,17 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Launchers (each returns the launch status).
 hipError_t launch_layout(const Geometry &g, const int32_t *idx, const epx_layout &L,
                          hipStream_t stream);
+// group < 0: every destination; else only group `group`'s rows.
 hipError_t launch_dispatch_bf16(const Geometry &g, const epx_layout &L, const void *x,
-                                int32_t hidden, void *recv, hipStream_t stream);
+                                int32_t hidden, void *recv, int group, hipStream_t stream);
 hipError_t launch_dispatch_fp8(const Geometry &g, const epx_layout &L, const void *x,
-                               int32_t hidden, void *recv, float *scales, hipStream_t stream);
+                               int32_t hidden, void *recv, float *scales, int group,
+                               hipStream_t stream);
 hipError_t launch_combine(const Geometry &g, const epx_layout &L, const void *y,
                           const float *w, int32_t hidden, void *out, hipStream_t stream);
+hipError_t launch_combine_group(const Geometry &g, const epx_layout &L, int group,
+                                const void *y, const float *w, int32_t hidden, float *carry,
+                                void *out, hipStream_t stream);
 hipError_t launch_f32_to_e4m3(const float *in, uint8_t *out, int64_t n, hipStream_t stream);
 hipError_t launch_relay_fanout(const Geometry &g, const epx_layout &L, const void *relay_rows,
                                const float *relay_scales, int64_t row_bytes, int nsc,

@@ -261,26 +261,74 @@ __global__ __launch_bounds__(256) void layout_scan_kernel(Geometry g, int32_t *_
         ws[(int64_t)ncol * g.Gs + col] = carry;
 }
 
+// ---------------------------------------------------------------- expert order
+// Rows are ordered by expert in the scan order of this function: expert ids
+// ascending, or with m > 1 expert groups (per-expert overlap) by (group,
+// rank, local index in the group), so that one group's rows form one range.
+__device__ __forceinline__ int expert_at(const Geometry &g, int q)
+{
+    if (g.m == 1)
+        return q;
+    const int per_group = g.R * g.epg;
+    const int grp = q / per_group;
+    const int rem = q - grp * per_group;
+    const int r = rem / g.epg;
+    return r * g.epr + grp * g.epg + (rem - r * g.epg);
+}
+
+// First row of block b = group * R + rank (b == m * R: the total), from the
+// final expert offsets eoff[0, E].
+__device__ __forceinline__ int block_start(const Geometry &g, const int32_t *eoff, int b)
+{
+    if (b >= g.m * g.R)
+        return eoff[g.E];
+    const int grp = b / g.R, r = b - grp * g.R;
+    return eoff[r * g.epr + grp * g.epg];
+}
+
+// Per-rank and per-group offsets from the final expert offsets (threads
+// [0, nthreads) of the workgroup): rank_offset (-1 with groups: a rank's rows
+// are then split over the groups), rank_rows and group_offset.
+__device__ void write_rank_and_group_offsets(const Geometry &g, const int32_t *eoff,
+                                             const epx_layout &L, int nthreads)
+{
+    const int tid = threadIdx.x;
+    for (int r = tid; r <= g.R; r += nthreads) {
+        L.rank_offset[r] = g.m == 1 ? eoff[r * g.epr] : -1;
+        if (r < g.R) {
+            int rows = 0;
+            for (int grp = 0; grp < g.m; ++grp)
+                rows += block_start(g, eoff, grp * g.R + r + 1) - block_start(g, eoff, grp * g.R + r);
+            L.rank_rows[r] = rows;
+        }
+    }
+    for (int b = tid; b <= g.m * g.R; b += nthreads)
+        L.group_offset[b] = block_start(g, eoff, b);
+}
+
 // ---------------------------------------------------------------- assign
 constexpr int kAssignThreads = 128;
 
-// Exclusive scan of src[0, n) (LDS) into dst[0, n] (LDS), dst[n] = total.
-__device__ void block_exclusive_scan(const int32_t *src, int32_t *dst, int n, int32_t *s_wsum)
+// Exclusive scan of the expert counts src[0, E) (LDS, by expert id) in the
+// row order of expert_at into dst[0, E] (LDS, by expert id), dst[E] = total.
+__device__ void block_exclusive_scan(const Geometry &g, const int32_t *src, int32_t *dst,
+                                     int32_t *s_wsum)
 {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, n = g.E;
     const int per = (n + kAssignThreads - 1) / kAssignThreads;
     const int beg = min(tid * per, n), end = min(beg + per, n);
     int sum = 0;
     for (int i = beg; i < end; ++i)
-        sum += src[i];
+        sum += src[expert_at(g, i)];
     const int incl = wave_inclusive_scan(sum);
     if (lane_id() == kWave - 1)
         s_wsum[tid / kWave] = incl;
     __syncthreads();
     int run = incl - sum + (tid >= kWave ? s_wsum[0] : 0);
     for (int i = beg; i < end; ++i) {
-        const int v = src[i];
-        dst[i] = run;
+        const int e = expert_at(g, i);
+        const int v = src[e];
+        dst[e] = run;
         run += v;
     }
     if (tid == kAssignThreads - 1)
@@ -346,7 +394,7 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
             L.totals[3] = bad;
         return;   // out-of-range ids: nothing else is defined
     }
-    block_exclusive_scan(s_tot, s_eoff, g.E, s_wsum);
+    block_exclusive_scan(g, s_tot, s_eoff, s_wsum);
     if (wave == 0) {
         const int v = lane < g.H ? s_tot[g.E + g.R + lane] : 0;
         const int incl = wave_inclusive_scan(v);
@@ -363,13 +411,9 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
             if (e < g.E)
                 L.expert_count[e] = s_tot[e];
         }
-        for (int r = tid; r <= g.R; r += kAssignThreads) {
-            L.rank_offset[r] = s_eoff[r * g.epr];
-            if (r < g.R) {
-                L.rank_rows[r] = s_eoff[(r + 1) * g.epr] - s_eoff[r * g.epr];
-                L.rank_tokens[r] = s_tot[g.E + r];
-            }
-        }
+        write_rank_and_group_offsets(g, s_eoff, L, kAssignThreads);
+        for (int r = tid; r < g.R; r += kAssignThreads)
+            L.rank_tokens[r] = s_tot[g.E + r];
         for (int h = tid; h <= g.H; h += kAssignThreads) {
             L.host_offset[h] = s_hoff[h];
             if (h < g.H) {
@@ -534,7 +578,8 @@ __global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
         }
     }
     __syncthreads();
-    const int cnt_e = tid < g.E ? s_eoff[tid] : 0;
+    const int e_q = tid < g.E ? expert_at(g, tid) : 0;   // expert at scan position tid
+    const int cnt_e = tid < g.E ? s_eoff[e_q] : 0;
     const int incl = wave_inclusive_scan(cnt_e);
     if (lane == kWave - 1)
         s_wsum[wave] = incl;
@@ -561,25 +606,20 @@ __global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
     __syncthreads();
     if (tid < g.E) {
         const int ex = incl - cnt_e + s_wsum[wave];
-        s_eoff[tid] = ex;
+        s_eoff[e_q] = ex;
         if (tid == g.E - 1)
             s_eoff[g.E] = ex + cnt_e;
     }
     __syncthreads();
 
     // global counts and offsets
-    for (int e = tid; e <= g.E; e += kSmallThreads) {
+    for (int e = tid; e <= g.E; e += kSmallThreads)
         L.expert_offset[e] = s_eoff[e];
-        if (e < g.E)
-            L.expert_count[e] = s_eoff[e + 1] - s_eoff[e];
-    }
-    for (int r = tid; r <= g.R; r += kSmallThreads) {
-        L.rank_offset[r] = s_eoff[r * g.epr];
-        if (r < g.R) {
-            L.rank_rows[r] = s_eoff[(r + 1) * g.epr] - s_eoff[r * g.epr];
-            L.rank_tokens[r] = s_rtok[r];
-        }
-    }
+    if (tid < g.E)
+        L.expert_count[e_q] = cnt_e;
+    write_rank_and_group_offsets(g, s_eoff, L, kSmallThreads);
+    for (int r = tid; r < g.R; r += kSmallThreads)
+        L.rank_tokens[r] = s_rtok[r];
     for (int h = tid; h <= g.H; h += kSmallThreads) {
         L.host_offset[h] = s_hoff[h];
         if (h < g.H) {

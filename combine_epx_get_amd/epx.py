@@ -31,13 +31,15 @@ STATUS = {0: "EPX_OK", 1: "EPX_ERR_ARG", 2: "EPX_ERR_INDEX", 3: "EPX_ERR_CAPACIT
 
 LAYOUT_FIELDS = ["expert_count", "expert_offset", "rank_rows", "rank_tokens", "rank_offset",
                  "host_tokens", "host_offset", "slot", "row_token", "relay_slot", "relay_token",
-                 "fanout_expert", "fanout_rank_mask", "relay_dst_rank", "totals", "workspace"]
+                 "fanout_expert", "fanout_rank_mask", "relay_dst_rank", "totals", "group_offset",
+                 "workspace"]
 RELAY_FIELDS = ("relay_slot", "relay_token", "fanout_expert", "fanout_rank_mask")
 
 
 class epx_problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("num_tokens", "topk", "num_experts", "num_ranks", "num_hosts", "my_rank", "mode")]
+                ("num_tokens", "topk", "num_experts", "num_ranks", "num_hosts", "my_rank", "mode",
+                 "num_groups")]
 
 
 class epx_layout(ctypes.Structure):
@@ -60,13 +62,17 @@ _lib.epx_combine_relay_partials.argtypes = [ctypes.POINTER(epx_problem), ctypes.
                                             ctypes.c_int64, _P]
 _lib.epx_combine_relay_finish.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_layout), _P,
                                           ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P]
+_lib.epx_dispatch_group.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_layout), ctypes.c_int32,
+                                    _P, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int64, _P]
+_lib.epx_combine_group.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_layout), ctypes.c_int32,
+                                   _P, ctypes.c_int64, _P, ctypes.c_int32, _P, _P, _P]
 _lib.epx_plan_swaps.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32,
                                 _P, _P, _P, _P, _P, _P]
 _lib.epx_status_string.argtypes = [ctypes.c_int]
 _lib.epx_status_string.restype = ctypes.c_char_p
 for _f in ("epx_layout_sizes", "epx_get_layout", "epx_dispatch", "epx_combine", "epx_read_error",
            "epx_f32_to_e4m3", "epx_relay_fanout", "epx_combine_relay_partials",
-           "epx_combine_relay_finish", "epx_plan_swaps"):
+           "epx_combine_relay_finish", "epx_plan_swaps", "epx_dispatch_group", "epx_combine_group"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.epx_abi_version.restype = ctypes.c_int32
 NARRAYS = len(LAYOUT_FIELDS)
@@ -89,8 +95,8 @@ def abi_version() -> int:
 
 
 def make_problem(num_tokens: int, topk: int, num_experts: int, num_ranks: int, num_hosts: int,
-                 my_rank: int = 0, mode: int = MODE_PER_EXPERT) -> epx_problem:
-    return epx_problem(num_tokens, topk, num_experts, num_ranks, num_hosts, my_rank, mode)
+                 my_rank: int = 0, mode: int = MODE_PER_EXPERT, num_groups: int = 1) -> epx_problem:
+    return epx_problem(num_tokens, topk, num_experts, num_ranks, num_hosts, my_rank, mode, num_groups)
 
 
 def epx_layout_sizes(problem: epx_problem) -> List[int]:
@@ -143,8 +149,7 @@ def epx_get_layout(problem: epx_problem, topk_idx: torch.Tensor, layout: Layout,
                                _stream(stream)), "epx_get_layout")
 
 
-def epx_dispatch(problem: epx_problem, layout: Layout, x: torch.Tensor, out_dtype: int,
-                 recv: torch.Tensor, recv_scales: Optional[torch.Tensor] = None, stream=None) -> None:
+def _dispatch_args(problem, x, out_dtype, recv, recv_scales):
     _need(x, torch.bfloat16, "x", 2)
     if x.shape[0] != problem.num_tokens:
         raise ValueError("x: first dimension must be num_tokens")
@@ -160,9 +165,25 @@ def epx_dispatch(problem: epx_problem, layout: Layout, x: torch.Tensor, out_dtyp
         scales_ptr = recv_scales.data_ptr()
     if recv.shape[1] != hidden:
         raise ValueError("recv: second dimension must be hidden")
+    return hidden, scales_ptr
+
+
+def epx_dispatch(problem: epx_problem, layout: Layout, x: torch.Tensor, out_dtype: int,
+                 recv: torch.Tensor, recv_scales: Optional[torch.Tensor] = None, stream=None) -> None:
+    hidden, scales_ptr = _dispatch_args(problem, x, out_dtype, recv, recv_scales)
     _check(_lib.epx_dispatch(ctypes.byref(problem), ctypes.byref(layout.struct), x.data_ptr(), hidden,
                              out_dtype, recv.data_ptr(), scales_ptr, recv.shape[0], _stream(stream)),
            "epx_dispatch")
+
+
+def epx_dispatch_group(problem: epx_problem, layout: Layout, group: int, x: torch.Tensor, out_dtype: int,
+                       recv: torch.Tensor, recv_scales: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Dispatch of one expert group's rows (recv is the whole [T*k, ...] buffer)."""
+    hidden, scales_ptr = _dispatch_args(problem, x, out_dtype, recv, recv_scales)
+    _check(_lib.epx_dispatch_group(ctypes.byref(problem), ctypes.byref(layout.struct), group, x.data_ptr(),
+                                   hidden, out_dtype, recv.data_ptr(), scales_ptr, recv.shape[0],
+                                   _stream(stream)),
+           "epx_dispatch_group")
 
 
 def epx_combine(problem: epx_problem, layout: Layout, y: torch.Tensor, topk_weights: torch.Tensor,
@@ -177,6 +198,29 @@ def epx_combine(problem: epx_problem, layout: Layout, y: torch.Tensor, topk_weig
     _check(_lib.epx_combine(ctypes.byref(problem), ctypes.byref(layout.struct), y.data_ptr(), y.shape[0],
                             topk_weights.data_ptr(), y.shape[1], out.data_ptr(), _stream(stream)),
            "epx_combine")
+
+
+def epx_combine_group(problem: epx_problem, layout: Layout, group: int, y: torch.Tensor,
+                      topk_weights: torch.Tensor, carry: Optional[torch.Tensor], out: torch.Tensor,
+                      stream=None) -> None:
+    """One expert group's combine; call for groups 0..m-1 in order on one
+    float32 [T, hidden] carry."""
+    _need(y, torch.bfloat16, "y", 2)
+    _need(topk_weights, torch.float32, "topk_weights", 2)
+    _need(out, torch.bfloat16, "out", 2)
+    if tuple(topk_weights.shape) != (problem.num_tokens, problem.topk):
+        raise ValueError("topk_weights: need [T, k]")
+    if tuple(out.shape) != (problem.num_tokens, y.shape[1]):
+        raise ValueError("out: need [T, hidden]")
+    if carry is not None:
+        _need(carry, torch.float32, "carry", 2)
+        if tuple(carry.shape) != tuple(out.shape):
+            raise ValueError("carry: need [T, hidden]")
+    _check(_lib.epx_combine_group(ctypes.byref(problem), ctypes.byref(layout.struct), group, y.data_ptr(),
+                                  y.shape[0], topk_weights.data_ptr(), y.shape[1],
+                                  carry.data_ptr() if carry is not None else None, out.data_ptr(),
+                                  _stream(stream)),
+           "epx_combine_group")
 
 
 def epx_read_error(layout: Layout, stream=None) -> int:

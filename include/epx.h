@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define EPX_ABI_VERSION 1
+#define EPX_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define EPX_API __attribute__((visibility("default")))
@@ -73,7 +73,14 @@ typedef enum { EPX_BF16 = 0, EPX_FP8_E4M3 = 1, EPX_F32 = 2 } epx_dtype;
 
 /* The problem of one source rank. Experts sit on ranks in contiguous
  * blocks (rank(e) = e / (num_experts/num_ranks)), ranks on hosts in
- * contiguous blocks (host(r) = r / (num_ranks/num_hosts)). */
+ * contiguous blocks (host(r) = r / (num_ranks/num_hosts)).
+ *
+ * Expert groups (per-expert overlap, digest section 3.3, Figure 4): with
+ * num_groups = m > 1 the experts are split into m groups that are dispatched
+ * and combined one after another; group g holds, on every rank, the local
+ * experts i = e mod (E/R) with i / (E/R/m) == g, so every rank has work in
+ * every group. m must divide E/R and the mode must be PER_EXPERT. 0 and 1
+ * both mean no groups. */
 typedef struct {
     int32_t num_tokens;   /* T: tokens of this source rank           */
     int32_t topk;         /* k: experts per token                     */
@@ -82,6 +89,7 @@ typedef struct {
     int32_t num_hosts;    /* H: hosts the ranks are spread over       */
     int32_t my_rank;      /* s: this source rank                      */
     int32_t mode;         /* epx_mode                                 */
+    int32_t num_groups;   /* m: expert groups (0 or 1: none)          */
 } epx_problem;
 
 /* Index of each layout array in the sizes reported by epx_layout_sizes. */
@@ -90,7 +98,7 @@ enum {
     EPX_L_EXPERT_OFFSET,     /* int32 [E+1]  exclusive prefix of expert_count                 */
     EPX_L_RANK_ROWS,         /* int32 [R]    copies per rank (sum over its experts)           */
     EPX_L_RANK_TOKENS,       /* int32 [R]    tokens with >= 1 expert on the rank              */
-    EPX_L_RANK_OFFSET,       /* int32 [R+1]  = expert_offset[r * E/R]                         */
+    EPX_L_RANK_OFFSET,       /* int32 [R+1]  = expert_offset[r * E/R]; -1 when m > 1          */
     EPX_L_HOST_TOKENS,       /* int32 [H]    tokens with >= 1 expert on the host (relay rows) */
     EPX_L_HOST_OFFSET,       /* int32 [H+1]  exclusive prefix of host_tokens                  */
     EPX_L_SLOT,              /* int32 [T*k]  per-expert row of pair (t, j)                    */
@@ -101,6 +109,7 @@ enum {
     EPX_L_FANOUT_RANK_MASK,  /* uint32 [C]   bit (rank mod R/H) for each local rank to feed   */
     EPX_L_RELAY_DST_RANK,    /* int32 [H]    same-index GPU: h*(R/H) + my_rank mod (R/H)     */
     EPX_L_TOTALS,            /* int32 [4]    rows, relay rows, max expert count, bad ids      */
+    EPX_L_GROUP_OFFSET,      /* int32 [m*R+1] first row of (group g, rank r) at g*R + r, total */
     EPX_L_WORKSPACE,         /* int32 [..]   scratch between the layout kernels (16-B aligned) */
     EPX_LAYOUT_NARRAYS
 };
@@ -108,6 +117,9 @@ enum {
 /* Device arrays of one layout. Row order (the digest fixes none):
  *  - per-expert rows: by expert, then token, then position j, so one
  *    expert's rows keep token order and one rank's rows are contiguous;
+ *    with m > 1 groups, by group first: rows by (group, expert, token, j),
+ *    so one group's rows are one range and, inside it, one rank's rows are
+ *    contiguous (group_offset); expert_offset follows that order;
  *  - relay rows: by host, then token; a token's own host gets a row too.
  * C = T * min(k, H) is the relay row capacity (batch x k sizing of the
  * digest, section 3.4). The four relay arrays are written in HOST_RELAY mode
@@ -128,6 +140,7 @@ typedef struct {
     uint32_t *fanout_rank_mask;
     int32_t *relay_dst_rank;
     int32_t *totals;
+    int32_t *group_offset;
     int32_t *workspace;
 } epx_layout;
 
@@ -166,6 +179,33 @@ EPX_API epx_status epx_dispatch(const epx_problem *p, const epx_layout *layout, 
 EPX_API epx_status epx_combine(const epx_problem *p, const epx_layout *layout, const void *y,
                        int64_t y_rows, const float *topk_weights, int32_t hidden, void *out,
                        void *stream);
+
+/* ---- Expert groups (per-expert overlap, digest section 3.3, Figure 4).
+ * The problem has num_groups = m > 1; call with group = 0 .. m-1.
+ *
+ * Dispatch of one group: epx_dispatch restricted to the pairs whose expert
+ * is in `group`: recv[slot[t,j]] = x[t] (bf16, or fp8 codes + scales) for
+ * those pairs only; rows of other groups are not touched. recv is the whole
+ * per-expert buffer (capacity_rows >= T*k); group g's rows are
+ * [group_offset[g*R], group_offset[(g+1)*R]). */
+EPX_API epx_status epx_dispatch_group(const epx_problem *p, const epx_layout *layout,
+                                      int32_t group, const void *x, int32_t hidden,
+                                      int32_t out_dtype, void *recv, float *recv_scales,
+                                      int64_t capacity_rows, void *stream);
+
+/* Combine of one group, in ascending group order on one carry: for every
+ * token with pairs in `group`, acc = (token had pairs in an earlier group) ?
+ * carry[t] : +0; then for j ascending with expert idx[t,j] in the group,
+ * acc = fmaf(w[t,j], y[slot[t,j]], acc); the result goes to carry[t]
+ * (float32 [T, hidden]) if the token has pairs in a later group, else to
+ * out[t] as bf16 (nearest even). After the last group every out row is
+ * written once. Tokens without pairs in the group are not touched. With
+ * m == 1 this is epx_combine and carry may be NULL. carry must be 16-byte
+ * aligned; y and weights as in epx_combine. */
+EPX_API epx_status epx_combine_group(const epx_problem *p, const epx_layout *layout,
+                                     int32_t group, const void *y, int64_t y_rows,
+                                     const float *topk_weights, int32_t hidden, float *carry,
+                                     void *out, void *stream);
 
 /* ---- Host relay, receive side and two-level combine (digest section 3.2,
  * Mode 2 with de-redundancy, Figure 3). Problem mode must be HOST_RELAY.

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(epx):
 
 
 def test_abi_version_and_status_strings(epx):
-    assert epx.abi_version() == 1
+    assert epx.abi_version() == 2
     for code in range(5):
         assert epx._lib.epx_status_string(code)
 
@@ -60,7 +60,11 @@ def test_layout_sizes(epx):
     assert s["relay_token"] == s["fanout_rank_mask"] == 4096 * 2
     assert s["fanout_expert"] == 4096 * 2 * 8
     assert s["totals"] == 4
+    assert s["group_offset"] == 16 + 1
     assert s["workspace"] == (64 + 1) * (256 + 16 + 2 + 1)     # 64 chunks of 64 tokens, + totals
+    pg = epx.make_problem(4096, 8, 256, 16, 2, 3, epx.MODE_PER_EXPERT, 4)
+    sg = dict(zip(epx.LAYOUT_FIELDS, epx.epx_layout_sizes(pg)))
+    assert sg["group_offset"] == 4 * 16 + 1 and sg["slot"] == 4096 * 8
     p0 = epx.make_problem(0, 2, 16, 4, 2)
     s0 = dict(zip(epx.LAYOUT_FIELDS, epx.epx_layout_sizes(p0)))
     assert s0["slot"] == 0 and s0["workspace"] == (4 + 1) * (16 + 4 + 2 + 1)   # columns padded to 4
@@ -80,6 +84,10 @@ def test_layout_sizes(epx):
     (10, 2, 16, 4, 2, 0, 7),      # bad mode
     (-1, 2, 16, 4, 2, 0, 0),      # negative T
     ((1 << 24) + 1, 2, 16, 4, 2, 0, 0),
+    (10, 2, 24, 4, 2, 0, 0, 4),   # 6 experts per rank, 4 groups
+    (10, 2, 16, 4, 2, 0, 1, 2),   # groups in relay mode
+    (10, 2, 16, 4, 2, 0, 0, -1),  # negative group count
+    (10, 2, 16, 4, 2, 0, 0, 8),   # more groups than experts per rank
 ])
 def test_bad_geometry_is_rejected_on_the_host(epx, geom):
     p = epx.make_problem(*geom)
@@ -161,6 +169,30 @@ def test_plan_swaps_host_checks(epx, args):
         ptrs[3] += 2
     c, i, o, lb, la, sw, hb = ptrs
     assert epx._lib.epx_plan_swaps(E, R, H, c, i, tau, o, lb, la, sw, hb, None) == 1
+
+
+def test_group_entry_host_checks(epx):
+    lib = epx._lib
+    by = ctypes.byref
+    A = 0x200000
+    p = epx.make_problem(64, 2, 16, 4, 2, 0, epx.MODE_PER_EXPERT, 2)
+    p1 = epx.make_problem(64, 2, 16, 4, 2, 0, epx.MODE_PER_EXPERT, 1)
+    L = _fake_layout(epx, relay=False)
+    assert lib.epx_dispatch_group(by(p), by(L), -1, A, 256, 0, A, None, 128, None) == 1
+    assert lib.epx_dispatch_group(by(p), by(L), 2, A, 256, 0, A, None, 128, None) == 1
+    assert lib.epx_dispatch_group(by(p), by(L), 0, A, 256, 0, A, None, 127, None) == 3
+    assert lib.epx_dispatch_group(by(p1), by(L), 1, A, 256, 0, A, None, 128, None) == 1
+    assert lib.epx_combine_group(by(p), by(L), 2, A, 128, A, 256, A, A, None) == 1
+    assert lib.epx_combine_group(by(p), by(L), -1, A, 128, A, 256, A, A, None) == 1
+    assert lib.epx_combine_group(by(p), by(L), 0, A, 128, A, 256, None, A, None) == 1      # no carry
+    assert lib.epx_combine_group(by(p), by(L), 0, A, 128, A, 256, A + 8, A, None) == 1     # misaligned
+    assert lib.epx_combine_group(by(p), by(L), 0, A, 127, A, 256, A, A, None) == 3
+    # the layout needs group_offset
+    ptrs = [0x100000 + 0x1000 * i for i in range(len(epx.LAYOUT_FIELDS))]
+    ptrs[epx.LAYOUT_FIELDS.index("group_offset")] = None
+    for n in epx.RELAY_FIELDS:
+        ptrs[epx.LAYOUT_FIELDS.index(n)] = None
+    assert lib.epx_get_layout(by(p), A, by(epx.epx_layout(*ptrs)), None) == 1
 
 
 def test_binding_rejects_wrong_tensors(epx):

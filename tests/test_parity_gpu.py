@@ -64,6 +64,8 @@ def assert_layout_parity(got, want, relay, what=""):
         assert g.shape == w.shape, (what, n, g.shape, w.shape)
         bad = np.nonzero(g.astype(np.int64) != w.astype(np.int64))[0]
         assert bad.size == 0, (what, n, int(bad[0]), g[bad[0]], w[bad[0]], bad.size)
+    if "group_offset" in got and "group_offset" not in want:   # one group: the rank offsets
+        assert np.array_equal(got["group_offset"], want["rank_offset"]), (what, "group_offset")
 
 
 def expert_outputs(tok_rows_f32: np.ndarray, idx: np.ndarray, slot: np.ndarray) -> np.ndarray:
