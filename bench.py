@@ -229,6 +229,9 @@ def main(argv=None) -> int:
     ap.add_argument("--groups", type=int, default=1, metavar="M",
                     help="expert groups (per-expert overlap): step = grouped layout, M group "
                          "dispatches, M group combines (per-expert mode)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed (layer time "
+                         "without per-launch host overhead)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -314,6 +317,9 @@ def main(argv=None) -> int:
         n_plans = [0]
 
     def step(ev=None):
+        # launches go to the current stream (a capture stream under --graph)
+        stream = torch.cuda.current_stream()
+
         def rec(i):
             if ev is not None:
                 ev[i].record(stream)
@@ -375,6 +381,31 @@ def main(argv=None) -> int:
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    graph_us = None
+    if args.graph:
+        if planner:
+            print("--graph does not capture the swap planner's alternating placement", file=sys.stderr)
+            return 2
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_us = g0.elapsed_time(g1) * 1e3 / args.steps
 
     lay_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     plan_ms = np.array([e[1].elapsed_time(e[6]) for e in evs])
@@ -461,6 +492,7 @@ def main(argv=None) -> int:
                    **({"swap_tau": args.swap_planner} if planner else {}),
                    **({"expert_groups": m} if m > 1 else {})},
         "us_per_layer": round(us_layer, 2),
+        **({"us_per_layer_graph": round(graph_us, 2)} if graph_us is not None else {}),
         "pct_of_peak_layer": round(100 * layer_bytes / (us_layer * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
         "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for n, v in per_kernel.items()},
