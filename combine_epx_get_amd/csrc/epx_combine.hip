@@ -35,13 +35,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f)
 __global__ __launch_bounds__(1024) void combine_kernel(
     const u32x4 *__restrict__ y, int nvec, int slice, const int32_t *__restrict__ slot,
     const float *__restrict__ w, int k, u32x4 *__restrict__ out,
-    const int32_t *__restrict__ totals)
+    const int32_t *__restrict__ totals, int64_t T)
 {
     __shared__ int32_t s_row[kMaxTopk];
     __shared__ float s_w[kMaxTopk];
-    if (totals[3] != 0)
-        return;   // the layout saw out-of-range expert ids
-    const int64_t t = blockIdx.x;
+    const int64_t t = item_index();
+    if (t >= T || totals[3] != 0)
+        return;   // past the last token, or the layout saw out-of-range expert ids
     const int c_beg = blockIdx.y * slice;
     const int c_end = min(nvec, c_beg + slice);
     if (threadIdx.x < k) {
@@ -109,14 +109,15 @@ __global__ __launch_bounds__(1024) void combine_kernel(
 __global__ __launch_bounds__(1024) void combine_group_kernel(
     const u32x4 *__restrict__ y, int nvec, int slice, const int32_t *__restrict__ slot,
     const float *__restrict__ w, int k, const int32_t *lo_p, const int32_t *hi_p,
-    float4 *__restrict__ carry, u32x4 *__restrict__ out, const int32_t *__restrict__ totals)
+    float4 *__restrict__ carry, u32x4 *__restrict__ out, const int32_t *__restrict__ totals,
+    int64_t T)
 {
     __shared__ int32_t s_row[kMaxTopk];
     __shared__ float s_w[kMaxTopk];
     __shared__ int32_t s_n, s_prior, s_later;
-    if (totals[3] != 0)
+    const int64_t t = item_index();
+    if (t >= T || totals[3] != 0)
         return;
-    const int64_t t = blockIdx.x;
     const int c_beg = blockIdx.y * slice;
     const int c_end = min(nvec, c_beg + slice);
     if (threadIdx.x < kWave) {   // k <= 64: one wave sees every pair
@@ -232,12 +233,12 @@ hipError_t launch_combine_group(const Geometry &g, const epx_layout &L, int grou
     const int nvec = hidden / 8;
     int slice, threads;
     combine_shape(g, nvec, slice, threads);
-    const dim3 grid(g.T, (nvec + slice - 1) / slice);
+    const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
     hipLaunchKernelGGL(combine_group_kernel, grid, dim3(threads), 0, stream, (const u32x4 *)y,
                        nvec, slice, (const int32_t *)L.slot, w, g.k,
                        (const int32_t *)L.group_offset + group * g.R,
                        (const int32_t *)L.group_offset + (group + 1) * g.R, (float4 *)carry,
-                       (u32x4 *)out, (const int32_t *)L.totals);
+                       (u32x4 *)out, (const int32_t *)L.totals, (int64_t)g.T);
     return hipGetLastError();
 }
 
@@ -247,10 +248,10 @@ hipError_t launch_combine(const Geometry &g, const epx_layout &L, const void *y,
     const int nvec = hidden / 8;
     int slice, threads;
     combine_shape(g, nvec, slice, threads);
-    const dim3 grid(g.T, (nvec + slice - 1) / slice);
+    const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
     hipLaunchKernelGGL(combine_kernel, grid, dim3(threads), 0, stream, (const u32x4 *)y, nvec,
                        slice, (const int32_t *)L.slot, w, g.k, (u32x4 *)out,
-                       (const int32_t *)L.totals);
+                       (const int32_t *)L.totals, (int64_t)g.T);
     return hipGetLastError();
 }
 

@@ -49,13 +49,13 @@ __device__ __forceinline__ void row_range(const int32_t *lo_p, const int32_t *hi
 __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     const u32x4 *__restrict__ x, int nvec, int slice, const int32_t *__restrict__ dest, int D,
     u32x4 *__restrict__ recv, const int32_t *__restrict__ totals, const int32_t *lo_p,
-    const int32_t *hi_p)
+    const int32_t *hi_p, int64_t T)
 {
-    if (totals[3] != 0)
-        return;   // the layout saw out-of-range expert ids
+    const int64_t t = item_index();
+    if (t >= T || totals[3] != 0)
+        return;   // past the last token, or the layout saw out-of-range expert ids
     int lo, hi;
     row_range(lo_p, hi_p, lo, hi);
-    const int64_t t = blockIdx.x;
     const int c_beg = blockIdx.y * slice;
     const int c_end = min(nvec, c_beg + slice);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -156,12 +156,12 @@ __device__ __forceinline__ uint32_t quantize4(float a, float b, float c, float d
 __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const u32x4 *__restrict__ x, int nvec, int slice, const int32_t *__restrict__ dest, int D,
     uint8_t *__restrict__ recv, float *__restrict__ scales, const int32_t *__restrict__ totals,
-    const int32_t *lo_p, const int32_t *hi_p)
+    const int32_t *lo_p, const int32_t *hi_p, int64_t T)
 {
     extern __shared__ u32x4 s_codes[];   // slice/2 vectors of 16 codes
-    if (totals[3] != 0)
+    const int64_t t = item_index();
+    if (t >= T || totals[3] != 0)
         return;
-    const int64_t t = blockIdx.x;
     int lo, hi;
     row_range(lo_p, hi_p, lo, hi);
     if (lo_p) {
@@ -283,10 +283,10 @@ hipError_t launch_dispatch_bf16(const Geometry &g, const epx_layout &L, const vo
     const int D = g.relay ? g.H : g.k;
     const int nvec = hidden / 8;
     const int slice = slice_width(g.T, nvec, kWave, 1 << 30, 2048);
-    const dim3 grid(g.T, (nvec + slice - 1) / slice);
+    const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
     hipLaunchKernelGGL(dispatch_bf16_kernel, grid, dim3(kThreads), 0, stream, (const u32x4 *)x,
                        nvec, slice, dest, D, (u32x4 *)recv, (const int32_t *)L.totals, lo_p,
-                       hi_p);
+                       hi_p, (int64_t)g.T);
     return hipGetLastError();
 }
 
@@ -306,11 +306,11 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const epx_layout &L, const voi
     // One group's dispatch writes about k/m rows per token.
     const int rows_per_token = group < 0 ? D : (D + g.m - 1) / g.m;
     const int slice = slice_width(g.T, nvec, 16, kMaxSliceVec, 2048 * rows_per_token);
-    const dim3 grid(g.T, (nvec + slice - 1) / slice);
+    const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
     const size_t lds = (size_t)slice * 8 + (size_t)(slice / 16) * sizeof(float);
     hipLaunchKernelGGL(dispatch_fp8_kernel, grid, dim3(kThreads), lds, stream, (const u32x4 *)x,
                        nvec, slice, dest, D, (uint8_t *)recv, scales, (const int32_t *)L.totals,
-                       lo_p, hi_p);
+                       lo_p, hi_p, (int64_t)g.T);
     return hipGetLastError();
 }
 

@@ -49,6 +49,23 @@ struct Geometry {
     FastDiv div_epr, div_rph, div_k;
 };
 
+// One workgroup per item (token or row) for any item count: item i runs as
+// blockIdx.x = i mod kGridX, blockIdx.z = i / kGridX (blockIdx.y stays free
+// for column slices), so that no grid dimension reaches 2^32 work-items.
+// Kernels return at once for i >= the item count (the last z-slab's tail).
+constexpr int kGridX = 65536;
+
+inline dim3 item_grid(int64_t items, int slices)
+{
+    return dim3((unsigned)(items < kGridX ? items : kGridX), (unsigned)slices,
+                (unsigned)((items + kGridX - 1) / kGridX));
+}
+
+__device__ __forceinline__ int64_t item_index()
+{
+    return (int64_t)blockIdx.z * kGridX + blockIdx.x;
+}
+
 // 16-byte and 8-byte native vectors (global_load/store_dwordx4, dwordx2).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

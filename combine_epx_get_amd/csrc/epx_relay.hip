@@ -70,9 +70,9 @@ __global__ __launch_bounds__(kThreads) void relay_fanout_kernel(
     __shared__ int32_t s_dst[kMaxTopk], s_j[kMaxTopk], s_n;
     if (L.totals[3] != 0)
         return;
-    const int64_t r = blockIdx.x;
+    const int64_t r = item_index();
     if (r >= L.totals[1])
-        return;   // past the relay rows in use
+        return;   // past the relay rows in use (also past the grid's last row)
     const int t = L.relay_token[r];
     const int n = fanout_list(L, k, r, t, s_dst, s_j, &s_n);
     const int c_beg = blockIdx.y * slice;
@@ -114,9 +114,9 @@ __global__ __launch_bounds__(kThreads) void relay_partials_kernel(
     __shared__ float s_w[kMaxTopk];
     if (L.totals[3] != 0)
         return;
-    const int64_t r = blockIdx.x;
+    const int64_t r = item_index();
     if (r >= L.totals[1])
-        return;
+        return;   // past the relay rows in use (also past the grid's last row)
     const int t = L.relay_token[r];
     const int n = fanout_list(L, k, r, t, s_dst, s_j, &s_n);
     if (threadIdx.x < n)
@@ -173,12 +173,12 @@ __global__ __launch_bounds__(kThreads) void relay_partials_kernel(
 template <bool BF16_IN>
 __global__ __launch_bounds__(kThreads) void relay_finish_kernel(
     const void *__restrict__ partials, int nvec, int slice, int H, epx_layout L,
-    u32x4 *__restrict__ out)
+    u32x4 *__restrict__ out, int64_t T)
 {
     __shared__ int32_t s_rows[kMaxHosts], s_n;
-    if (L.totals[3] != 0)
+    const int64_t t = item_index();
+    if (t >= T || L.totals[3] != 0)
         return;
-    const int64_t t = blockIdx.x;
     if (threadIdx.x < kWave) {
         const int h = threadIdx.x;
         const int r = h < H ? L.relay_slot[t * H + h] : -1;
@@ -245,7 +245,7 @@ hipError_t launch_relay_fanout(const Geometry &g, const epx_layout &L, const voi
     const int64_t cap = (int64_t)g.T * (g.k < g.H ? g.k : g.H);
     const int row_vec = (int)(row_bytes / 16);
     const int slice = slices_for(cap, row_vec, kWave, 2048);
-    const dim3 grid((unsigned)cap, (row_vec + slice - 1) / slice);
+    const dim3 grid = item_grid(cap, (row_vec + slice - 1) / slice);
     hipLaunchKernelGGL(relay_fanout_kernel, grid, dim3(kThreads), 0, stream,
                        (const u32x4 *)relay_rows, relay_scales, row_vec, nsc, slice, g.k, L,
                        (u32x4 *)recv, recv_scales);
@@ -259,7 +259,7 @@ hipError_t launch_relay_partials(const Geometry &g, const epx_layout &L, const v
     const int64_t cap = (int64_t)g.T * (g.k < g.H ? g.k : g.H);
     const int nvec = hidden / 8;
     const int slice = slices_for(cap, nvec, kWave, 2048);
-    const dim3 grid((unsigned)cap, (nvec + slice - 1) / slice);
+    const dim3 grid = item_grid(cap, (nvec + slice - 1) / slice);
     if (bf16_out)
         hipLaunchKernelGGL(relay_partials_kernel<true>, grid, dim3(kThreads), 0, stream,
                            (const u32x4 *)y, nvec, slice, w, g.k, L, partials);
@@ -274,13 +274,13 @@ hipError_t launch_relay_finish(const Geometry &g, const epx_layout &L, const voi
 {
     const int nvec = hidden / 8;
     const int slice = slices_for(g.T, nvec, kWave, 2048);
-    const dim3 grid(g.T, (nvec + slice - 1) / slice);
+    const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
     if (bf16_in)
         hipLaunchKernelGGL(relay_finish_kernel<true>, grid, dim3(kThreads), 0, stream, partials,
-                           nvec, slice, g.H, L, (u32x4 *)out);
+                           nvec, slice, g.H, L, (u32x4 *)out, (int64_t)g.T);
     else
         hipLaunchKernelGGL(relay_finish_kernel<false>, grid, dim3(kThreads), 0, stream, partials,
-                           nvec, slice, g.H, L, (u32x4 *)out);
+                           nvec, slice, g.H, L, (u32x4 *)out, (int64_t)g.T);
     return hipGetLastError();
 }
 
