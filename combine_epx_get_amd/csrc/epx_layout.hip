@@ -30,24 +30,47 @@ namespace {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-__device__ __forceinline__ int wave_inclusive_scan(int v)
+// DPP lane moves (gfx9): row_shr:n moves each 16-lane row's values n lanes
+// up (lanes below n in the row read 0: bound_ctrl); row_bcast:15 / 31 hand
+// lane 15 / 31 to the next row(s), written only where row_mask allows.
+constexpr int kDppRowShr = 0x110;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xf, bool BOUND_ZERO = true>
+__device__ __forceinline__ int dpp(int v)
 {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        int n = __shfl_up(v, d, kWave);
-        if (lane >= d)
-            v += n;
-    }
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, BOUND_ZERO);
+}
+
+// Inclusive scan within each 16-lane row.
+__device__ __forceinline__ int row_inclusive_scan(int v)
+{
+    v += dpp<kDppRowShr + 1>(v);
+    v += dpp<kDppRowShr + 2>(v);
+    v += dpp<kDppRowShr + 4>(v);
+    v += dpp<kDppRowShr + 8>(v);
     return v;
 }
 
+__device__ __forceinline__ int wave_inclusive_scan(int v)
+{
+    v = row_inclusive_scan(v);
+    v += dpp<kDppRowBcast15, 0xa, false>(v);   // rows 1 and 3 add the end of rows 0 and 2
+    v += dpp<kDppRowBcast31, 0xc, false>(v);   // rows 2 and 3 add the end of rows 0-1
+    return v;
+}
+
+// Maximum over the wave (values >= 0), the same in every lane.
 __device__ __forceinline__ int wave_max(int v)
 {
-#pragma unroll
-    for (int d = kWave / 2; d > 0; d >>= 1)
-        v = max(v, __shfl_xor(v, d, kWave));
-    return v;
+    v = max(v, dpp<kDppRowShr + 1>(v));
+    v = max(v, dpp<kDppRowShr + 2>(v));
+    v = max(v, dpp<kDppRowShr + 4>(v));
+    v = max(v, dpp<kDppRowShr + 8>(v));
+    v = max(v, dpp<kDppRowBcast15, 0xa, false>(v));
+    v = max(v, dpp<kDppRowBcast31, 0xc, false>(v));
+    return __builtin_amdgcn_readlane(v, kWave - 1);
 }
 
 // Lanes whose `e` equals mine among the active lanes (ballot multisplit).
@@ -116,79 +139,6 @@ __device__ __forceinline__ void count_pair(int p, const Geometry &g, const int32
         atomicAdd(&s_htok[h], 1);
 }
 
-// Relay rows of one token on one lane of a wave holding up to 64 consecutive
-// tokens: for each host, rows of the tokens that touch it, in token order,
-// from `base(h)` on. Every lane of the wave must call it (ballots). KR > 0:
-// the token's ids, ranks and hosts are held in registers (k <= KR).
-template <int KR, typename Base>
-__device__ __forceinline__ void relay_rows(bool act, int t, const int32_t *ids, const int32_t *rks,
-                                           const int32_t *hks, const Geometry &g, Base base,
-                                           const epx_layout &L)
-{
-    const uint64_t below = (1ull << lane_id()) - 1ull;
-    constexpr int N = KR > 0 ? KR : 1;
-    int e_[N], r_[N], h_[N];
-    uint64_t hosts = 0;
-    if (KR > 0) {
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-            const bool v = act && j < g.k;
-            e_[j] = v ? ids[j] : -1;
-            r_[j] = v ? rks[j] : 0;
-            h_[j] = v ? hks[j] : -1;
-            if (v)
-                hosts |= 1ull << h_[j];
-        }
-    } else if (act) {
-        for (int j = 0; j < g.k; ++j)
-            hosts |= 1ull << hks[j];
-    }
-    for (int h = 0; h < g.H; ++h) {
-        const bool has = (hosts >> h) & 1ull;
-        const uint64_t bal = __ballot(has);
-        if (!act)
-            continue;
-        if (!has) {
-            L.relay_slot[(int64_t)t * g.H + h] = -1;
-            continue;
-        }
-        const int r = base(h) + __popcll(bal & below);
-        L.relay_slot[(int64_t)t * g.H + h] = r;
-        L.relay_token[r] = t;
-        int32_t *fan = L.fanout_expert + (int64_t)r * g.k;
-        uint32_t mask = 0;
-        if (KR > 0) {
-#pragma unroll
-            for (int j = 0; j < N; ++j)
-                if (j < g.k) {
-                    const bool here = h_[j] == h;
-                    fan[j] = here ? e_[j] : -1;
-                    if (here)
-                        mask |= 1u << (r_[j] - h * g.rph);
-                }
-        } else {
-            for (int j = 0; j < g.k; ++j) {
-                const bool here = hks[j] == h;
-                fan[j] = here ? ids[j] : -1;
-                if (here)
-                    mask |= 1u << (rks[j] - h * g.rph);
-            }
-        }
-        L.fanout_rank_mask[r] = mask;
-    }
-}
-
-template <typename Base>
-__device__ __forceinline__ void relay_rows_any(bool act, int t, const int32_t *ids,
-                                               const int32_t *rks, const int32_t *hks,
-                                               const Geometry &g, Base base, const epx_layout &L)
-{
-    if (g.k <= kRegK)
-        relay_rows<kRegK>(act, t, ids, rks, hks, g, base, L);
-    else
-        relay_rows<0>(act, t, ids, rks, hks, g, base, L);
-}
-
 // Relay rows past the used ones, [used, capacity) split over `parts`, read as empty.
 __device__ __forceinline__ void clear_relay_tail(const Geometry &g, int64_t used, int part,
                                                  int parts, int nthreads, const epx_layout &L)
@@ -202,6 +152,65 @@ __device__ __forceinline__ void clear_relay_tail(const Geometry &g, int64_t used
     }
     for (int64_t i = beg * g.k + threadIdx.x; i < end * g.k; i += nthreads)
         L.fanout_expert[i] = -1;
+}
+
+// Relay rows of up to 64 consecutive tokens (one per lane: token t, its
+// pairs at s_idx/s_rk/s_hk + i*k and its host mask at s_hmask[i] for the
+// lane's local index i) for host h: rows in token order from `base`; the
+// fan-out row is written with 16-byte stores when it is aligned. Every lane
+// of the wave must call it (ballot).
+__device__ __forceinline__ void relay_item(bool act, int t, int i, int h, const Geometry &g,
+                                           const int32_t *s_idx, const int32_t *s_hk,
+                                           const int32_t *s_rk, const uint64_t *s_hmask,
+                                           int base, const epx_layout &L)
+{
+    const int lane = lane_id();
+    const bool has = act && ((s_hmask[act ? i : 0] >> h) & 1ull);
+    const uint64_t bal = __ballot(has);
+    if (!act)
+        return;
+    if (!has) {
+        L.relay_slot[(int64_t)t * g.H + h] = -1;
+        return;
+    }
+    const int r = base + __popcll(bal & ((1ull << lane) - 1ull));
+    L.relay_slot[(int64_t)t * g.H + h] = r;
+    L.relay_token[r] = t;
+    const int32_t *ids = s_idx + i * g.k, *hks = s_hk + i * g.k, *rks = s_rk + i * g.k;
+    int32_t *fan = L.fanout_expert + (int64_t)r * g.k;
+    uint32_t mask = 0;
+    if ((g.k & 3) == 0 && ((uintptr_t)L.fanout_expert & 15) == 0) {
+        for (int j = 0; j < g.k; j += 4) {
+            int4 v;
+            v.x = hks[j] == h ? ids[j] : -1;
+            v.y = hks[j + 1] == h ? ids[j + 1] : -1;
+            v.z = hks[j + 2] == h ? ids[j + 2] : -1;
+            v.w = hks[j + 3] == h ? ids[j + 3] : -1;
+            *(int4 *)(fan + j) = v;
+        }
+    } else {
+        for (int j = 0; j < g.k; ++j)
+            fan[j] = hks[j] == h ? ids[j] : -1;
+    }
+    for (int j = 0; j < g.k; ++j)
+        if (hks[j] == h)
+            mask |= 1u << (rks[j] - h * g.rph);
+    L.fanout_rank_mask[r] = mask;
+}
+
+// Host mask of each of the np / k tokens staged at s_hk (threads [0, nthreads)).
+__device__ __forceinline__ void token_host_masks(int ntok, const Geometry &g, const int32_t *s_hk,
+                                                 uint64_t *s_hmask, int nthreads)
+{
+    for (int i = threadIdx.x; i < ntok; i += nthreads) {
+        uint64_t hosts = 0;
+        for (int j = 0; j < g.k; ++j) {
+            const int h = s_hk[i * g.k + j];
+            if (h >= 0)
+                hosts |= 1ull << h;
+        }
+        s_hmask[i] = hosts;
+    }
 }
 
 // ---------------------------------------------------------------- count
@@ -307,14 +316,19 @@ __device__ void write_rank_and_group_offsets(const Geometry &g, const int32_t *e
 }
 
 // ---------------------------------------------------------------- assign
-constexpr int kAssignThreads = 128;
+constexpr int kAssignThreads = 512;
+constexpr int kAssignWaves = kAssignThreads / kWave;
+// Up to this many workgroups the assign kernel sums the count columns itself
+// (no scan launch); measured on MI355X, 64 workgroups summing 64-entry
+// columns cost more than the scan launch they save.
+constexpr int kSumsMaxG = 16;
 
 // Exclusive scan of the expert counts src[0, E) (LDS, by expert id) in the
 // row order of expert_at into dst[0, E] (LDS, by expert id), dst[E] = total.
 __device__ void block_exclusive_scan(const Geometry &g, const int32_t *src, int32_t *dst,
                                      int32_t *s_wsum)
 {
-    const int tid = threadIdx.x, n = g.E;
+    const int tid = threadIdx.x, n = g.E, wave = tid / kWave;
     const int per = (n + kAssignThreads - 1) / kAssignThreads;
     const int beg = min(tid * per, n), end = min(beg + per, n);
     int sum = 0;
@@ -322,9 +336,11 @@ __device__ void block_exclusive_scan(const Geometry &g, const int32_t *src, int3
         sum += src[expert_at(g, i)];
     const int incl = wave_inclusive_scan(sum);
     if (lane_id() == kWave - 1)
-        s_wsum[tid / kWave] = incl;
+        s_wsum[wave] = incl;
     __syncthreads();
-    int run = incl - sum + (tid >= kWave ? s_wsum[0] : 0);
+    int run = incl - sum;
+    for (int w = 0; w < wave; ++w)
+        run += s_wsum[w];
     for (int i = beg; i < end; ++i) {
         const int e = expert_at(g, i);
         const int v = src[e];
@@ -338,41 +354,52 @@ __device__ void block_exclusive_scan(const Geometry &g, const int32_t *src, int3
 // SUMS: this workgroup sums the raw count columns itself (total and the
 // prefix over workgroups before it); otherwise the scan kernel has left the
 // prefix in place and the totals after the columns.
+//
+// The chunk's pairs are split over the first nww waves in (t, j) order
+// (nww = 8, fewer when the per-wave count table would not fit in LDS); each
+// of them counts its pairs per expert, a scan over these waves gives each its
+// first row per expert, and they then assign their rows at once. Relay rows
+// are assigned host by host, one host per wave.
 template <bool SUMS>
 __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
-    const int32_t *__restrict__ idx, Geometry g, const int32_t *__restrict__ ws, epx_layout L)
+    const int32_t *__restrict__ idx, Geometry g, const int32_t *__restrict__ ws, epx_layout L,
+    int nww)
 {
-    extern __shared__ int32_t lds[];
+    extern __shared__ __align__(16) int32_t lds[];
     const int ncol = g.E + g.R + g.H + 1;
     const int kc = g.ct * g.k;
-    int32_t *s_tot = lds;                  // [ncol] column totals
+    const int cs = g.E + 1;                // padded per-wave stride (distinct LDS banks)
+    uint64_t *s_hmask = (uint64_t *)lds;   // [ct] hosts each token touches
+    int32_t *s_tot = lds + 2 * g.ct;       // [ncol] column totals
     int32_t *s_pre = s_tot + ncol;         // [ncol] this workgroup's prefix per column
     int32_t *s_eoff = s_pre + ncol;        // [E + 1]
     int32_t *s_hoff = s_eoff + g.E + 1;    // [H + 1]
-    int32_t *s_idx = s_hoff + g.H + 1;     // [64 k] ids, ranks, hosts of the chunk
+    int32_t *s_idx = s_hoff + g.H + 1;     // [kc] ids, ranks, hosts of the chunk
     int32_t *s_rk = s_idx + kc;
     int32_t *s_hk = s_rk + kc;
-    __shared__ int32_t s_wsum[2];
-    __shared__ int32_t s_wmax[2];
+    int32_t *s_wc = s_hk + kc;             // [nww][cs] per-wave counts, then wave bases
+    __shared__ int32_t s_wsum[kAssignWaves];
+    __shared__ int32_t s_wmax[kAssignWaves];
 
     const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int t0 = b * g.ct;
     const int nt = max(0, min(g.ct, g.T - t0));
+    const int np = nt * g.k;
     const int64_t p0 = (int64_t)t0 * g.k;
+    const uint64_t below = (1ull << lane) - 1ull;
 
-    stage_pairs(idx, p0, nt * g.k, g, s_idx, s_rk, s_hk, kAssignThreads);
+    stage_pairs(idx, p0, np, g, s_idx, s_rk, s_hk, kAssignThreads);
+    for (int i = tid; i < nww * cs; i += kAssignThreads)
+        s_wc[i] = 0;
     if (SUMS) {
-        // each thread sums whole columns as 16-byte vectors (Gs % 4 == 0);
-        // G <= 16 here, so a column is at most 4 vectors, all loaded at once
+        // each thread sums whole columns as 16-byte vectors (Gs % 4 == 0;
+        // entries [G, Gs) are padding, never written)
         for (int c = tid; c < ncol; c += kAssignThreads) {
             const int4 *col = (const int4 *)(ws + (int64_t)c * g.Gs);
             int tot = 0, pre = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (4 * i >= g.Gs)
-                    break;
+            for (int i = 0; 4 * i < g.Gs; ++i) {
                 const int4 v = col[i];
-                const int i0 = 4 * i;   // entries [G, Gs) are padding, never written
+                const int i0 = 4 * i;
                 tot += (i0 < g.G ? v.x : 0) + (i0 + 1 < g.G ? v.y : 0) +
                        (i0 + 2 < g.G ? v.z : 0) + (i0 + 3 < g.G ? v.w : 0);
                 pre += (i0 < b ? v.x : 0) + (i0 + 1 < b ? v.y : 0) + (i0 + 2 < b ? v.z : 0) +
@@ -394,7 +421,22 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
             L.totals[3] = bad;
         return;   // out-of-range ids: nothing else is defined
     }
-    block_exclusive_scan(g, s_tot, s_eoff, s_wsum);
+
+    // per-wave counts per expert (the first lane of each group adds its size)
+    const int per_wave = (np + nww * kWave - 1) / (nww * kWave) * kWave;
+    const int pw0 = wave < nww ? wave * per_wave : np;
+    const int pw1 = wave < nww ? min(np, pw0 + per_wave) : np;
+    for (int base = pw0; base < pw1; base += kWave) {
+        const int p = base + lane;
+        const bool act = p < pw1;
+        const int e = act ? s_idx[p] : 0;
+        const uint64_t peers = match_peers(act, e, g.nbits);
+        if (act && (peers & below) == 0ull)
+            s_wc[wave * cs + e] += __popcll(peers);
+    }
+    if (g.relay)
+        token_host_masks(nt, g, s_hk, s_hmask, kAssignThreads);
+    block_exclusive_scan(g, s_tot, s_eoff, s_wsum);   // synchronises the workgroup
     if (wave == 0) {
         const int v = lane < g.H ? s_tot[g.E + g.R + lane] : 0;
         const int incl = wave_inclusive_scan(v);
@@ -402,6 +444,16 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
             s_hoff[lane] = incl - v;
         if (lane == kWave - 1)
             s_hoff[g.H] = incl;
+    }
+    // each wave's first row per expert: the expert's offset, the rows of
+    // earlier workgroups, then those of earlier waves
+    for (int e = tid; e < g.E; e += kAssignThreads) {
+        int run = s_pre[e];
+        for (int w = 0; w < nww; ++w) {
+            const int v = s_wc[w * cs + e];
+            s_wc[w * cs + e] = run;
+            run += v;
+        }
     }
     __syncthreads();
 
@@ -429,41 +481,38 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
             s_wmax[wave] = m;
         __syncthreads();
         if (tid == 0) {
+            int mm = 0;
+            for (int w = 0; w < kAssignWaves; ++w)
+                mm = max(mm, s_wmax[w]);
             L.totals[0] = g.T * g.k;
             L.totals[1] = s_hoff[g.H];
-            L.totals[2] = max(s_wmax[0], s_wmax[1]);
+            L.totals[2] = mm;
             L.totals[3] = 0;
         }
     }
 
-    if (wave == 0) {
-        // rows per expert in (t, j) order: base = offset + rows of earlier workgroups
-        for (int e = lane; e < g.E; e += kWave)
-            s_eoff[e] += s_pre[e];
-        const uint64_t below = (1ull << lane) - 1ull;
-        const int np = nt * g.k;
-        for (int base = 0; base < np; base += kWave) {
-            const int p = base + lane;
-            const bool act = p < np;
-            const int e = act ? s_idx[p] : 0;
-            const uint64_t peers = match_peers(act, e, g.nbits);
-            if (act) {
-                const int before = __popcll(peers & below);
-                const int first = s_eoff[e];
-                const int row = first + before;
-                L.slot[p0 + p] = row;
-                L.row_token[row] = t0 + g.div_k.div(p);
-                if (before == 0)
-                    s_eoff[e] = first + __popcll(peers);
-            }
+    // rows per expert in (t, j) order
+    for (int base = pw0; base < pw1; base += kWave) {
+        const int p = base + lane;
+        const bool act = p < pw1;
+        const int e = act ? s_idx[p] : 0;
+        const uint64_t peers = match_peers(act, e, g.nbits);
+        if (act) {
+            const int before = __popcll(peers & below);
+            const int rel = s_wc[wave * cs + e];
+            const int row = s_eoff[e] + rel + before;
+            L.slot[p0 + p] = row;
+            L.row_token[row] = t0 + g.div_k.div(p);
+            if (before == 0)
+                s_wc[wave * cs + e] = rel + __popcll(peers);
         }
-    } else if (g.relay) {
-        const int o = lane * g.k;
-        relay_rows_any(lane < nt, t0 + lane, s_idx + o, s_rk + o, s_hk + o, g,
-                   [&](int h) { return s_hoff[h] + s_pre[g.E + g.R + h]; }, L);
     }
-    if (g.relay)
-        clear_relay_tail(g, s_hoff[g.H], b, g.G, kAssignThreads, L);
+    if (!g.relay)
+        return;
+    for (int h = wave; h < g.H; h += kAssignWaves)
+        relay_item(lane < nt, t0 + lane, lane, h, g, s_idx, s_hk, s_rk, s_hmask,
+                   s_hoff[h] + s_pre[g.E + g.R + h], L);
+    clear_relay_tail(g, s_hoff[g.H], b, g.G, kAssignThreads, L);
 }
 
 // ---------------------------------------------------------------- single workgroup
@@ -475,21 +524,26 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
 // rows exactly as the multi-workgroup path does.
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / kWave;
+static_assert(kSmallWaves == 16, "per-wave columns are scanned by 16-lane groups");
 
 __global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
     const int32_t *__restrict__ idx, Geometry g, epx_layout L)
 {
-    extern __shared__ int32_t lds[];
+    extern __shared__ __align__(16) int32_t lds[];
     const int P = g.T * g.k;
-    int32_t *s_idx = lds;                              // [P] ids, ranks, hosts
+    uint64_t *s_hmask = (uint64_t *)lds;               // [T] hosts each token touches
+    int32_t *s_idx = lds + 2 * g.T;                    // [P] ids, ranks, hosts
     int32_t *s_rk = s_idx + P;
     int32_t *s_hk = s_rk + P;
-    int32_t *s_cnt = s_hk + P;                         // [waves][E] counts, then row bases
-    int32_t *s_eoff = s_cnt + kSmallWaves * g.E;       // [E + 1]
+    // per-wave columns are padded to an odd stride so that the 16 cells of a
+    // column sit in 16 different LDS banks
+    const int cs = g.E + 1, hs = g.H + 1;
+    int32_t *s_cnt = s_hk + P;                         // [waves][cs] counts, then wave bases
+    int32_t *s_eoff = s_cnt + kSmallWaves * cs;        // [E + 1]
     int32_t *s_rtok = s_eoff + g.E + 1;                // [R]
     int32_t *s_htok = s_rtok + g.R;                    // [H]
-    int32_t *s_hcnt = s_htok + g.H;                    // [waves][H] counts, then relay bases
-    int32_t *s_hoff = s_hcnt + kSmallWaves * g.H;      // [H + 1]
+    int32_t *s_hcnt = s_htok + g.H;                    // [waves][hs] counts, then wave bases
+    int32_t *s_hoff = s_hcnt + kSmallWaves * hs;       // [H + 1]
     __shared__ int32_t s_bad;
     __shared__ int32_t s_wsum[kSmallWaves];
     __shared__ int32_t s_wmax[kSmallWaves];
@@ -498,7 +552,7 @@ __global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
     const uint64_t below = (1ull << lane) - 1ull;
 
     stage_pairs(idx, 0, P, g, s_idx, s_rk, s_hk, kSmallThreads);
-    for (int i = tid; i < kSmallWaves * g.E; i += kSmallThreads)
+    for (int i = tid; i < kSmallWaves * cs; i += kSmallThreads)
         s_cnt[i] = 0;
     for (int i = tid; i < g.R; i += kSmallThreads)
         s_rtok[i] = 0;
@@ -518,7 +572,7 @@ __global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
         const bool ok = act && s_rk[p] >= 0;
         const uint64_t peers = match_peers(ok, e, g.nbits);
         if (ok && (peers & below) == 0ull)
-            s_cnt[wave * g.E + e] += __popcll(peers);
+            s_cnt[wave * cs + e] += __popcll(peers);
     }
     // bad ids, distinct ranks and hosts per token
     for (int p = tid; p < P; p += kSmallThreads) {
@@ -528,29 +582,41 @@ __global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
             continue;
         }
         const int first = g.div_k.div(p) * g.k;
+        const int jp = p - first;
         const int h = s_hk[p];
         bool new_rank = true, new_host = true;
-        for (int q = first; q < p; ++q) {
-            new_rank = new_rank && s_rk[q] != r;
-            new_host = new_host && s_hk[q] != h;
+        if (g.k <= kRegK) {
+#pragma unroll
+            for (int q = 0; q < kRegK - 1; ++q)
+                if (q < jp) {
+                    new_rank = new_rank && s_rk[first + q] != r;
+                    new_host = new_host && s_hk[first + q] != h;
+                }
+        } else {
+            for (int q = first; q < p; ++q) {
+                new_rank = new_rank && s_rk[q] != r;
+                new_host = new_host && s_hk[q] != h;
+            }
         }
         if (new_rank)
             atomicAdd(&s_rtok[r], 1);
         if (new_host)
             atomicAdd(&s_htok[h], 1);
     }
-    // per-wave relay counts: tokens of wave w touching host h
+    // hosts of each token, and per-wave relay counts: tokens of wave w touching host h
     uint64_t hosts = 0;
-    if (tid < g.T)
+    if (tid < g.T) {
         for (int j = 0; j < g.k; ++j) {
             const int h = s_hk[tid * g.k + j];
             if (h >= 0)
                 hosts |= 1ull << h;
         }
+        s_hmask[tid] = hosts;
+    }
     for (int h = 0; h < g.H; ++h) {
         const uint64_t bal = __ballot((hosts >> h) & 1ull);
         if (lane == 0)
-            s_hcnt[wave * g.H + h] = __popcll(bal);
+            s_hcnt[wave * hs + h] = __popcll(bal);
     }
     __syncthreads();
     if (s_bad != 0) {
@@ -559,23 +625,16 @@ __global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
         return;   // out-of-range ids: nothing else is defined
     }
 
-    // scans over waves: each wave's base per expert / per host, and totals
-    if (tid < g.E) {
-        int run = 0;
-        for (int w = 0; w < kSmallWaves; ++w) {
-            const int c = s_cnt[w * g.E + tid];
-            s_cnt[w * g.E + tid] = run;
-            run += c;
-        }
-        s_eoff[tid] = run;
-    } else if (tid >= kSmallThreads - kWave && tid - (kSmallThreads - kWave) < g.H) {
-        const int h = tid - (kSmallThreads - kWave);
-        int run = 0;
-        for (int w = 0; w < kSmallWaves; ++w) {
-            const int c = s_hcnt[w * g.H + h];
-            s_hcnt[w * g.H + h] = run;
-            run += c;
-        }
+    // per column (expert, then host) an exclusive scan over the 16 waves by a
+    // 16-lane group; the expert totals land in s_eoff
+    for (int c = tid / kSmallWaves; c < g.E + g.H; c += kSmallThreads / kSmallWaves) {
+        const int w = tid % kSmallWaves;
+        int32_t *cell = c < g.E ? s_cnt + w * cs + c : s_hcnt + w * hs + (c - g.E);
+        const int v = *cell;
+        const int incl = row_inclusive_scan(v);   // the 16-lane group is one DPP row
+        *cell = incl - v;
+        if (w == kSmallWaves - 1 && c < g.E)
+            s_eoff[c] = incl;
     }
     __syncthreads();
     const int e_q = tid < g.E ? expert_at(g, tid) : 0;   // expert at scan position tid
@@ -633,12 +692,9 @@ __global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
         L.totals[2] = s_wmax[0];
         L.totals[3] = 0;
     }
-    for (int w = 0; w < kSmallWaves; ++w)
-        for (int e = tid; e < g.E; e += kSmallThreads)
-            s_cnt[w * g.E + e] += s_eoff[e];
-    __syncthreads();
 
-    // ordered walk: rows of each expert in (t, j) order
+    // ordered walk: rows of each expert in (t, j) order, from the expert's
+    // offset plus the rows of earlier waves
     for (int base = pw0; base < pw1; base += kWave) {
         const int p = base + lane;
         const bool act = p < pw1;
@@ -646,19 +702,23 @@ __global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
         const uint64_t peers = match_peers(act, e, g.nbits);
         if (act) {
             const int before = __popcll(peers & below);
-            const int first = s_cnt[wave * g.E + e];
-            const int row = first + before;
+            const int rel = s_cnt[wave * cs + e];
+            const int row = s_eoff[e] + rel + before;
             L.slot[p] = row;
             L.row_token[row] = g.div_k.div(p);
             if (before == 0)
-                s_cnt[wave * g.E + e] = first + __popcll(peers);
+                s_cnt[wave * cs + e] = rel + __popcll(peers);
         }
     }
     if (!g.relay)
         return;
-    const int o = (tid < g.T ? tid : 0) * g.k;
-    relay_rows_any(tid < g.T, tid, s_idx + o, s_rk + o, s_hk + o, g,
-               [&](int h) { return s_hoff[h] + s_hcnt[wave * g.H + h]; }, L);
+    // relay rows: one (64-token chunk, host) item per wave
+    const int nchunk = (g.T + kWave - 1) / kWave;
+    for (int it = wave; it < nchunk * g.H; it += kSmallWaves) {
+        const int c = it / g.H, h = it - c * g.H;
+        const int t = c * kWave + lane_id();
+        relay_item(t < g.T, t, t, h, g, s_idx, s_hk, s_rk, s_hmask, s_hoff[h] + s_hcnt[c * hs + h], L);
+    }
     clear_relay_tail(g, s_hoff[g.H], 0, 1, kSmallThreads, L);
 }
 
@@ -669,8 +729,8 @@ size_t small_layout_lds(const Geometry &g)
 {
     if (g.T > kSmallThreads || g.T * g.k > 4096 || g.E > 512)
         return 0;
-    const size_t ints = 3 * (size_t)g.T * g.k + (size_t)kSmallWaves * g.E + g.E + 1 + g.R + g.H +
-                        (size_t)kSmallWaves * g.H + g.H + 1;
+    const size_t ints = 2 * (size_t)g.T + 3 * (size_t)g.T * g.k + (size_t)kSmallWaves * (g.E + 1) +
+                        g.E + 1 + g.R + g.H + (size_t)kSmallWaves * (g.H + 1) + g.H + 1;
     const size_t bytes = ints * sizeof(int32_t);
     return bytes <= 64 * 1024 ? bytes : 0;
 }
@@ -694,10 +754,19 @@ hipError_t launch_layout(const Geometry &g, const int32_t *idx, const epx_layout
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    const size_t lds_assign = (size_t)(2 * ncol + g.E + 1 + g.H + 1 + 3 * kc) * sizeof(int32_t);
-    if (g.G <= 16) {
+    // counting waves: 8, halved until the assign workgroup's LDS fits in 64 KB
+    int nww = kAssignWaves;
+    size_t lds_assign = 0;
+    for (;;) {
+        lds_assign = (size_t)(2 * g.ct + 2 * ncol + g.E + 1 + g.H + 1 + 3 * kc + nww * (g.E + 1)) *
+                     sizeof(int32_t);
+        if (lds_assign <= 64 * 1024 || nww == 1)
+            break;
+        nww /= 2;
+    }
+    if (g.G <= kSumsMaxG) {
         hipLaunchKernelGGL(layout_assign_kernel<true>, dim3(g.G), dim3(kAssignThreads), lds_assign,
-                           stream, idx, g, (const int32_t *)L.workspace, L);
+                           stream, idx, g, (const int32_t *)L.workspace, L, nww);
         return hipGetLastError();
     }
     const int cols_per_block = 256 / kWave;
@@ -707,7 +776,7 @@ hipError_t launch_layout(const Geometry &g, const int32_t *idx, const epx_layout
     if (err != hipSuccess)
         return err;
     hipLaunchKernelGGL(layout_assign_kernel<false>, dim3(g.G), dim3(kAssignThreads), lds_assign,
-                       stream, idx, g, (const int32_t *)L.workspace, L);
+                       stream, idx, g, (const int32_t *)L.workspace, L, nww);
     return hipGetLastError();
 }
 
