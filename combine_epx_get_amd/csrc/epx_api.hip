@@ -39,7 +39,7 @@ epx_status make_geometry(const epx_problem *p, Geometry *g)
     g->s = s;
     g->epr = E / R;
     g->rph = R / H;
-    g->ct = k <= 16 ? 64 : epx::kChunkPairs / k;
+    g->ct = k <= 16 ? 32 : epx::kChunkPairs / k;
     g->G = T > 0 ? (T + g->ct - 1) / g->ct : 1;
     g->Gs = (g->G + 3) & ~3;
     g->div_epr.init(g->epr);

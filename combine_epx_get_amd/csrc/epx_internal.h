@@ -39,7 +39,7 @@ struct Geometry {
     int32_t T, k, E, R, H, s;
     int32_t epr;     // experts per rank
     int32_t rph;     // ranks per host
-    int32_t ct;      // tokens per layout workgroup: min(64, kChunkPairs / k)
+    int32_t ct;      // tokens per layout workgroup: 32 (k <= 16), else kChunkPairs / k
     int32_t G;       // layout workgroups = max(1, ceil(T / ct))
     int32_t Gs;      // workspace column stride: G rounded up to 4 (16-byte columns)
     int32_t nbits;   // bits that distinguish expert ids (ceil(log2 E))

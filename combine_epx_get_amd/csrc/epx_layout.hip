@@ -9,17 +9,19 @@
 // per-rank token counts are those of the DeepEP issue "[GH-ISSUE #250]
 // Profiling when rank unbalance".
 //
-// Row order: per-expert rows by (expert, token, j); relay rows by (host,
-// token). Positions come from ordered wave walks, never from atomic order:
-// a wave takes 64 pairs at a time in (t, j) order, groups equal expert ids
-// with ceil(log2 E) ballots (a wave-level multisplit) and gives each lane
-// base + popcount(peers below it); the group's first lane then advances the
-// base. Counting may use LDS atomics, because counts do not depend on order.
+// Row order: per-expert rows by (expert, token, j) -- with expert groups by
+// (group, expert, token, j); relay rows by (host, token). Positions come
+// from ordered wave walks, never from atomic order: a wave takes 64 pairs at
+// a time in (t, j) order, groups equal expert ids with ceil(log2 E) ballots
+// (a wave-level multisplit) and gives each lane base + popcount(peers below
+// it); the group's first lane then advances the base. Counting may use LDS
+// atomics, because counts do not depend on order.
 //
 // Three shapes, no global atomics and no zero-filled buffers:
 //   small batches (<= 4096 pairs): one workgroup does everything in LDS;
-//   up to 16 workgroups of up to 64 tokens: count, then assign (each assign
-//     workgroup sums the count columns itself);
+//   up to 16 workgroups of up to 32 tokens (k <= 16; 1024 / k tokens
+//     above): count, then assign (each assign workgroup sums the count
+//     columns itself);
 //   more: count, a column scan (one wave per counter), assign.
 // Every per-pair rank and host is computed once, with division constants
 // prepared on the host, and staged in LDS with the chunk's ids.

@@ -61,7 +61,7 @@ def test_layout_sizes(epx):
     assert s["fanout_expert"] == 4096 * 2 * 8
     assert s["totals"] == 4
     assert s["group_offset"] == 16 + 1
-    assert s["workspace"] == (64 + 1) * (256 + 16 + 2 + 1)     # 64 chunks of 64 tokens, + totals
+    assert s["workspace"] == (128 + 1) * (256 + 16 + 2 + 1)    # 128 chunks of 32 tokens, + totals
     pg = epx.make_problem(4096, 8, 256, 16, 2, 3, epx.MODE_PER_EXPERT, 4)
     sg = dict(zip(epx.LAYOUT_FIELDS, epx.epx_layout_sizes(pg)))
     assert sg["group_offset"] == 4 * 16 + 1 and sg["slot"] == 4096 * 8
