@@ -261,3 +261,21 @@ def test_imbalance_ratio_constructed():
     idx = (np.arange(T * k) % E).astype(np.int32).reshape(T, k)
     lay = oracle.layout(idx, E, R, H, 0)
     assert lay["totals"][2] / (T * k / E) == 1.0    # 128 copies over 64 experts: 2 each
+
+
+def test_relay_rows_reproduce_the_hybridep_rdma_counter():
+    """The HybridEP log prints 117.11 MB of RDMA sends per rank for its BF16
+    dispatch (4096 tokens, hidden 7168, top-8, 128 experts on 16 ranks over 2
+    nodes). One bf16 row per (token, destination host), the token's own host
+    included, reproduces it; remote hosts alone would give half."""
+    g = json.load(open(os.path.join(GOLDEN, "hybridep_bf16_counters.json")))
+    T, k, E, R, H, h = g["tokens"], g["topk"], g["num_experts"], g["num_ranks"], g["num_hosts"], g["hidden"]
+    rng = np.random.Generator(np.random.PCG64(590))
+    idx = W.draw_routing(rng, T, E, k, "uniform")
+    lay = oracle.layout(idx, E, R, H, 0, relay=True)
+    rows = int(lay["totals"][1])
+    assert rows == int(lay["host_tokens"].sum())
+    mb = rows * h * 2 / 1e6
+    assert abs(mb - g["rdma_send_MB"]) / g["rdma_send_MB"] < 0.005, mb
+    remote_only = rows - T + int(np.sum(~np.any(idx // (E // R) // (R // H) == 0, axis=1)))
+    assert abs(remote_only * h * 2 / 1e6 - g["rdma_send_MB"] / 2) / (g["rdma_send_MB"] / 2) < 0.01
