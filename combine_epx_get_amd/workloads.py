@@ -66,6 +66,9 @@ class Workload:
 # The five workloads: a tiny parity case, two decode shapes (uniform and
 # skewed), the 4096-token large batch and the fp8 outlier batch. A Zipf(0.6)
 # decode variant gives imbalance ratios inside the digest's measured range.
+# The rank_* shapes are the source ranks of the DeepEP rank-imbalance issue
+# (2 machines x 8 ranks): 384 tokens per rank on machine 1 and 64 on machine
+# 2, against 224 everywhere when balanced.
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload("tiny", 64, 256, 16, 2, 4, 2, "uniform",
                      modes=("per_expert", "relay"), dtypes=("bf16", "fp8"), seed=1),
@@ -79,6 +82,12 @@ WORKLOADS: Dict[str, Workload] = {
                             modes=("per_expert",), seed=4),
     "fp8_dispatch": Workload("fp8_dispatch", 4096, 7168, 256, 8, 32, 4, "zipf", zipf_s=1.0,
                              outlier_frac=0.01, modes=("relay",), dtypes=("fp8",), seed=5),
+    "rank_heavy": Workload("rank_heavy", 384, 7168, 256, 8, 16, 2, "uniform",
+                           modes=("per_expert", "relay"), seed=6, my_rank=3),
+    "rank_light": Workload("rank_light", 64, 7168, 256, 8, 16, 2, "uniform",
+                           modes=("per_expert", "relay"), seed=7, my_rank=11),
+    "rank_balanced": Workload("rank_balanced", 224, 7168, 256, 8, 16, 2, "uniform",
+                              modes=("per_expert", "relay"), seed=8, my_rank=11),
 }
 
 
