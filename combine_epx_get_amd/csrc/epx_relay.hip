@@ -169,7 +169,30 @@ __global__ __launch_bounds__(kThreads) void relay_partials_kernel(
     }
 }
 
-// Finish: lanes own 8 channels of the token's output row.
+// Finish: lanes own 8 channels in each of kFinChunks 16-byte chunks of the
+// token's output row; the loads of up to kFinBatch partial rows are issued
+// before the first add (the adds then run in ascending host order).
+constexpr int kFinChunks = 2;
+constexpr int kFinBatch = 4;
+
+template <bool BF16_IN>
+__device__ __forceinline__ void load_partial(const void *partials, int64_t r, int nvec, int c,
+                                             float p[8])
+{
+    if (BF16_IN) {
+        const u32x4 v = __builtin_nontemporal_load((const u32x4 *)partials + r * nvec + c);
+        p[0] = bf16_lo(v.x); p[1] = bf16_hi(v.x); p[2] = bf16_lo(v.y); p[3] = bf16_hi(v.y);
+        p[4] = bf16_lo(v.z); p[5] = bf16_hi(v.z); p[6] = bf16_lo(v.w); p[7] = bf16_hi(v.w);
+    } else {
+        const u32x4 *src = (const u32x4 *)partials + (r * nvec + c) * 2;
+        const u32x4 a = __builtin_nontemporal_load(src), b = __builtin_nontemporal_load(src + 1);
+        p[0] = __uint_as_float(a.x); p[1] = __uint_as_float(a.y);
+        p[2] = __uint_as_float(a.z); p[3] = __uint_as_float(a.w);
+        p[4] = __uint_as_float(b.x); p[5] = __uint_as_float(b.y);
+        p[6] = __uint_as_float(b.z); p[7] = __uint_as_float(b.w);
+    }
+}
+
 template <bool BF16_IN>
 __global__ __launch_bounds__(kThreads) void relay_finish_kernel(
     const void *__restrict__ partials, int nvec, int slice, int H, epx_layout L,
@@ -192,36 +215,46 @@ __global__ __launch_bounds__(kThreads) void relay_finish_kernel(
     const int n = s_n;
     const int c_beg = blockIdx.y * slice;
     const int c_end = min(nvec, c_beg + slice);
-    for (int c = c_beg + threadIdx.x; c < c_end; c += kThreads) {
-        float acc[8];
+    for (int c0 = c_beg + threadIdx.x; c0 < c_end; c0 += kThreads * kFinChunks) {
+        float acc[kFinChunks][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            acc[i] = 0.0f;
-        for (int q = 0; q < n; ++q) {
-            const int64_t r = s_rows[q];
-            float p[8];
-            if (BF16_IN) {
-                const u32x4 v = __builtin_nontemporal_load((const u32x4 *)partials + r * nvec + c);
-                p[0] = bf16_lo(v.x); p[1] = bf16_hi(v.x); p[2] = bf16_lo(v.y); p[3] = bf16_hi(v.y);
-                p[4] = bf16_lo(v.z); p[5] = bf16_hi(v.z); p[6] = bf16_lo(v.w); p[7] = bf16_hi(v.w);
-            } else {
-                const u32x4 *src = (const u32x4 *)partials + (r * nvec + c) * 2;
-                const u32x4 a = __builtin_nontemporal_load(src), b = __builtin_nontemporal_load(src + 1);
-                p[0] = __uint_as_float(a.x); p[1] = __uint_as_float(a.y);
-                p[2] = __uint_as_float(a.z); p[3] = __uint_as_float(a.w);
-                p[4] = __uint_as_float(b.x); p[5] = __uint_as_float(b.y);
-                p[6] = __uint_as_float(b.z); p[7] = __uint_as_float(b.w);
+        for (int i = 0; i < kFinChunks; ++i)
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                acc[i][q] = 0.0f;
+        for (int q0 = 0; q0 < n; q0 += kFinBatch) {
+            float p[kFinBatch][kFinChunks][8];
+#pragma unroll
+            for (int qq = 0; qq < kFinBatch; ++qq)
+#pragma unroll
+                for (int i = 0; i < kFinChunks; ++i) {
+                    const int c = c0 + i * kThreads;
+                    if (q0 + qq < n && c < c_end)
+                        load_partial<BF16_IN>(partials, s_rows[q0 + qq], nvec, c, p[qq][i]);
+                }
+#pragma unroll
+            for (int qq = 0; qq < kFinBatch; ++qq) {
+                if (q0 + qq >= n)
+                    break;
+#pragma unroll
+                for (int i = 0; i < kFinChunks; ++i)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[i][e] = acc[i][e] + p[qq][i][e];
             }
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                acc[i] = acc[i] + p[i];
         }
-        u32x4 o;
-        o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-        o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-        o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-        o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
-        __builtin_nontemporal_store(o, out + t * nvec + c);
+#pragma unroll
+        for (int i = 0; i < kFinChunks; ++i) {
+            const int c = c0 + i * kThreads;
+            if (c >= c_end)
+                continue;
+            u32x4 o;
+            o.x = f32_to_bf16(acc[i][0]) | (f32_to_bf16(acc[i][1]) << 16);
+            o.y = f32_to_bf16(acc[i][2]) | (f32_to_bf16(acc[i][3]) << 16);
+            o.z = f32_to_bf16(acc[i][4]) | (f32_to_bf16(acc[i][5]) << 16);
+            o.w = f32_to_bf16(acc[i][6]) | (f32_to_bf16(acc[i][7]) << 16);
+            __builtin_nontemporal_store(o, out + t * nvec + c);
+        }
     }
 }
 
