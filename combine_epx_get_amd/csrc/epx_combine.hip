@@ -2,8 +2,8 @@
 //
 // Combine gathers each token's k expert results back and sums them (digest
 // "Balancing and Beyond: Communication-Centric Optimizations in Expert
-// Parallelism", section 3.2 "Combine sums", and section 3.4: combine buffers
-// hold batch x k rows). The sum is weighted by the gate weights, accumulated
+// Parallelism", section 3.2, the combine step, and section 3.4: combine
+// buffers hold batch x k rows). The sum is weighted by the gate weights, accumulated
 // in float32 as acc = fma(w_j, y_j, acc) for j = 0..k-1 from +0 and rounded
 // once to bf16, nearest even: the same order on every element, so results
 // are deterministic and independent of the launch shape.

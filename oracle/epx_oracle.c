@@ -26,7 +26,7 @@
  *    section 3.1). Format OCP E4M3FN (largest finite value 448), one float32
  *    scale per 128 channels equal to the block's max |x| / 448.
  *  - Combine: gather each token's k expert outputs and sum them with the gate
- *    weights (digest section 3.2, "Combine sums", and section 3.4, combine
+ *    weights (digest section 3.2, the combine step, and section 3.4, combine
  *    buffers sized batch x k), accumulated in float32 with fmaf in ascending
  *    j from +0, rounded once to bf16 (nearest, ties to even).
  *  - Relay receive side and two-level combine (digest section 3.2, Mode 2,
