@@ -279,3 +279,44 @@ def test_relay_rows_reproduce_the_hybridep_rdma_counter():
     assert abs(mb - g["rdma_send_MB"]) / g["rdma_send_MB"] < 0.005, mb
     remote_only = rows - T + int(np.sum(~np.any(idx // (E // R) // (R // H) == 0, axis=1)))
     assert abs(remote_only * h * 2 / 1e6 - g["rdma_send_MB"] / 2) / (g["rdma_send_MB"] / 2) < 0.01
+
+
+# ---------------------------------------------------------------- property sweep
+from hypothesis import HealthCheck, given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+
+@st.composite
+def _geometry_and_routing(draw):
+    """Small geometries across the edge cases: T = 0 or 1, k = 1 or k = E,
+    E = R, H = 1, H = R, one expert for every pair, repeated ids in a row."""
+    H = draw(st.integers(1, 4))
+    rph = draw(st.integers(1, 3))
+    R = H * rph
+    epr = draw(st.integers(1, 3))
+    E = R * epr
+    k = draw(st.integers(1, min(E, 5)))
+    T = draw(st.integers(0, 12))
+    s = draw(st.integers(0, R - 1))
+    kind = draw(st.sampled_from(["any", "one_expert", "distinct"]))
+    if kind == "one_expert":
+        e = draw(st.integers(0, E - 1))
+        idx = [[e] * k for _ in range(T)]
+    elif kind == "distinct":
+        idx = [draw(st.permutations(list(range(E))))[:k] for _ in range(T)]
+    else:
+        idx = [[draw(st.integers(0, E - 1)) for _ in range(k)] for _ in range(T)]
+    return np.array(idx, np.int32).reshape(T, k), E, R, H, s
+
+
+@settings(max_examples=150, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(_geometry_and_routing())
+def test_layout_property_sweep(case):
+    idx, E, R, H, s = case
+    got = oracle.layout(idx, E, R, H, s, relay=True)
+    want = brute_layout(idx, E, R, H, s)
+    assert_layout_equal(got, want, ["expert_count", "expert_offset", "rank_rows", "rank_offset",
+                                    "rank_tokens", "host_tokens", "host_offset", "slot", "row_token",
+                                    "relay_dst_rank", "totals", "relay_slot", "relay_token",
+                                    "fanout_expert", "fanout_rank_mask"])

@@ -294,3 +294,30 @@ def test_e4m3_conversion_exhaustive_vs_oracle(epx):
     dq = torch.empty(v.size, dtype=torch.uint8, device="cuda")
     epx.epx_f32_to_e4m3(_dev(v), dq)
     assert np.array_equal(dq.cpu().numpy(), oracle.f32_to_e4m3(v))
+
+
+# ---------------------------------------------------------------- equivalences
+@pytest.mark.parametrize("name,relay", [("tiny", True), ("decode_skewed", False), ("fp8_dispatch", True)])
+def test_fused_fp8_equals_quantising_the_bf16_rows(epx, name, relay):
+    """The fp8 dispatch (quantised once per token, stored to every row) equals
+    the bf16 dispatch followed by quantising each dispatched row on its own."""
+    w = W.WORKLOADS[name]
+    d = W.make_inputs(w)
+    T, k, h = d["T"], w.topk, w.hidden
+    p = epx.make_problem(T, k, w.num_experts, w.num_ranks, w.num_hosts, w.my_rank,
+                         epx.MODE_HOST_RELAY if relay else epx.MODE_PER_EXPERT)
+    L = epx.Layout(p)
+    epx.epx_get_layout(p, _dev(d["topk_idx"]), L)
+    cap = epx.relay_capacity(p) if relay else T * k
+    rows = int(L["totals"].cpu().numpy()[1 if relay else 0])
+    x = _bf16_dev(d["x"])
+    rb = torch.empty((cap, h), dtype=torch.bfloat16, device="cuda")
+    epx.epx_dispatch(p, L, x, epx.BF16, rb)
+    q = torch.empty((cap, h), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((cap, h // 128), dtype=torch.float32, device="cuda")
+    epx.epx_dispatch(p, L, x, epx.FP8_E4M3, q, sc)
+    bf_rows = _bits(rb)[:rows]
+    ident = {"slot": np.arange(rows, dtype=np.int32), "totals": np.array([rows, 0, 0, 0], np.int32)}
+    wq, wsc = oracle.dispatch_fp8(bf_rows, ident, 1, 1, False)
+    assert np.array_equal(q.cpu().numpy()[:rows], wq), name
+    assert np.array_equal(sc.cpu().numpy()[:rows].view(np.uint32), wsc.view(np.uint32)), name
