@@ -169,6 +169,9 @@ SHAPES = [
     (3000, 16, 2048, 64, 2, 33, 256, "uniform"),  # largest E, 32 ranks per host
     (50, 64, 64, 8, 4, 1, 128, "uniform"),      # largest k
     (5000, 8, 256, 256, 64, 200, 128, "uniform"),  # 64 hosts, 1 expert per rank
+    (200, 32, 64, 8, 4, 2, 136, "zipf"),        # k > 16 in the multi-workgroup layout (32-token chunks)
+    (100, 64, 128, 16, 8, 3, 128, "uniform"),   # k = 64 there: 16-token chunks, assign sums columns
+    (1500, 24, 96, 12, 3, 7, 128, "zipf"),      # k = 24: 42-token chunks, 36 workgroups, scan kernel
 ]
 
 

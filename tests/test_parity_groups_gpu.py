@@ -113,6 +113,7 @@ SHAPES = [
     (50, 64, 64, 8, 4, 1, 4, 128),
     (5000, 8, 256, 16, 2, 5, 4, 128),
     (300, 8, 64, 8, 1, 0, 1, 512),      # one group
+    (1500, 24, 96, 12, 3, 7, 4, 128),   # k = 24 in the multi-workgroup layout
 ]
 
 

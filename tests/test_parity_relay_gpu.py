@@ -100,6 +100,9 @@ SHAPES = [
     (3000, 16, 2048, 64, 2, 33, 256),
     (50, 64, 64, 8, 4, 1, 128),
     (5000, 8, 256, 256, 64, 200, 128),
+    (200, 32, 64, 8, 4, 2, 136),      # k > 16 in the multi-workgroup layout
+    (100, 64, 128, 16, 8, 3, 128),
+    (1500, 24, 96, 12, 3, 7, 128),
 ]
 
 
