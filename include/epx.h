@@ -148,13 +148,25 @@ typedef struct {
  * Host only; returns EPX_ERR_ARG for an unsupported problem. */
 EPX_API epx_status epx_layout_sizes(const epx_problem *p, int64_t sizes_out[EPX_LAYOUT_NARRAYS]);
 
-/* Counts, offsets and row positions for topk_idx [T, k] (int32, row-major).
- * The layout arrays are overwritten (no zeroing needed beforehand); the
- * workspace is scratch owned by the caller for the duration of the call. */
+/* Counts, offsets and row positions for topk_idx [T, k] (int32, row-major):
+ * copies per expert and per rank, distinct tokens per rank and per host
+ * (digest sections 1-2; the per-rank receive counts of the DeepEP issue
+ * "[GH-ISSUE #250] Profiling when rank unbalance"), their prefixes, the row
+ * of every (token, expert) pair and, in HOST_RELAY mode, of every (token,
+ * destination host) copy with its fan-out index (digest section 3.2, Mode 2,
+ * Figure 3). The layout arrays are overwritten (no zeroing needed
+ * beforehand); the workspace is scratch owned by the caller for the duration
+ * of the call. Errors: EPX_ERR_ARG on the host (problem, pointers); ids
+ * outside [0, E) are counted into totals[3] on the device and the other
+ * arrays are then undefined (epx_read_error reports it). */
 EPX_API epx_status epx_get_layout(const epx_problem *p, const int32_t *topk_idx,
                           const epx_layout *layout, void *stream);
 
-/* Scatter token rows into the layout's destination rows.
+/* Scatter token rows into the layout's destination rows: one copy per
+ * destination expert (PER_EXPERT, the digest's Mode 1) or one copy per
+ * destination host (HOST_RELAY, Mode 2 with de-redundancy; digest section
+ * 3.2), optionally converted from bf16 to fp8 inside the dispatch (section
+ * 3.1).
  *  x            bf16 [T, hidden], row-major
  *  out_dtype    EPX_BF16: recv is bf16 [capacity_rows, hidden];
  *               EPX_FP8_E4M3: recv is uint8 codes [capacity_rows, hidden] and
@@ -166,16 +178,22 @@ EPX_API epx_status epx_get_layout(const epx_problem *p, const int32_t *topk_idx,
  *  hidden       multiple of 8 (bf16) or of 128 (fp8)
  *  capacity_rows >= T*k (PER_EXPERT) or >= T*min(k, H) (HOST_RELAY)
  * Rows are written at the layout's slots (PER_EXPERT) or relay slots
- * (HOST_RELAY); other rows of recv are left untouched. */
+ * (HOST_RELAY); other rows of recv are left untouched. Errors: EPX_ERR_ARG
+ * (dtype, hidden, pointers, 16-byte alignment), EPX_ERR_CAPACITY (recv too
+ * small); after a layout that saw bad ids nothing is written. */
 EPX_API epx_status epx_dispatch(const epx_problem *p, const epx_layout *layout, const void *x,
                         int32_t hidden, int32_t out_dtype, void *recv, float *recv_scales,
                         int64_t capacity_rows, void *stream);
 
-/* out[t, :] = bf16( sum_j topk_weights[t, j] * y[slot[t, j], :] ): the k
+/* Combine (digest section 3.2, the combine step; section 3.4, buffers of
+ * batch x k rows):
+ * out[t, :] = bf16( sum_j topk_weights[t, j] * y[slot[t, j], :] ): the k
  * expert outputs of each token gathered from the per-expert rows of y
  * (bf16 [y_rows, hidden], y_rows >= T*k) and summed in float32 as
  * acc = fma(w, y, acc) for j = 0..k-1 from +0, rounded to bf16 (nearest
- * even). Weights are used as given. hidden must be a multiple of 8. */
+ * even). Weights are used as given. hidden must be a multiple of 8.
+ * Errors: EPX_ERR_ARG (hidden, pointers, alignment), EPX_ERR_CAPACITY
+ * (y_rows < T*k); after a layout that saw bad ids nothing is written. */
 EPX_API epx_status epx_combine(const epx_problem *p, const epx_layout *layout, const void *y,
                        int64_t y_rows, const float *topk_weights, int32_t hidden, void *out,
                        void *stream);
