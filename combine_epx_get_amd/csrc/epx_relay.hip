@@ -103,8 +103,13 @@ __global__ __launch_bounds__(kThreads) void relay_fanout_kernel(
     }
 }
 
-// Partials: lanes own 8 channels (one 16-byte bf16 vector of y); fp32 output
-// is two 16-byte vectors per lane, bf16 one.
+// Partials: lanes own 8 channels (one 16-byte bf16 vector of y) in each of
+// kParChunks chunks; the loads of up to kParBatch expert rows for all of a
+// lane's chunks are issued before the first fma. fp32 output is two 16-byte
+// vectors per chunk, bf16 one.
+constexpr int kParChunks = 4;
+constexpr int kParBatch = 4;
+
 template <bool BF16_OUT>
 __global__ __launch_bounds__(kThreads) void relay_partials_kernel(
     const u32x4 *__restrict__ y, int nvec, int slice, const float *__restrict__ w, int k,
@@ -124,56 +129,76 @@ __global__ __launch_bounds__(kThreads) void relay_partials_kernel(
     __syncthreads();
     const int c_beg = blockIdx.y * slice;
     const int c_end = min(nvec, c_beg + slice);
-    for (int c = c_beg + threadIdx.x; c < c_end; c += kThreads) {
-        float acc[8];
+    for (int c0 = c_beg + threadIdx.x; c0 < c_end; c0 += kThreads * kParChunks) {
+        float acc[kParChunks][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            acc[i] = 0.0f;
-        for (int j0 = 0; j0 < n; j0 += 8) {
-            u32x4 v[8];
+        for (int i = 0; i < kParChunks; ++i)
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-                if (j0 + jj < n)
-                    v[jj] = __builtin_nontemporal_load(y + (int64_t)s_dst[j0 + jj] * nvec + c);
+            for (int q = 0; q < 8; ++q)
+                acc[i][q] = 0.0f;
+        for (int j0 = 0; j0 < n; j0 += kParBatch) {
+            u32x4 v[kParBatch][kParChunks];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
+            for (int jj = 0; jj < kParBatch; ++jj)
+#pragma unroll
+                for (int i = 0; i < kParChunks; ++i) {
+                    const int c = c0 + i * kThreads;
+                    if (j0 + jj < n && c < c_end)
+                        v[jj][i] = __builtin_nontemporal_load(y + (int64_t)s_dst[j0 + jj] * nvec + c);
+                }
+#pragma unroll
+            for (int jj = 0; jj < kParBatch; ++jj) {
                 if (j0 + jj >= n)
                     break;
                 const float wj = s_w[j0 + jj];
-                acc[0] = __builtin_fmaf(wj, bf16_lo(v[jj].x), acc[0]);
-                acc[1] = __builtin_fmaf(wj, bf16_hi(v[jj].x), acc[1]);
-                acc[2] = __builtin_fmaf(wj, bf16_lo(v[jj].y), acc[2]);
-                acc[3] = __builtin_fmaf(wj, bf16_hi(v[jj].y), acc[3]);
-                acc[4] = __builtin_fmaf(wj, bf16_lo(v[jj].z), acc[4]);
-                acc[5] = __builtin_fmaf(wj, bf16_hi(v[jj].z), acc[5]);
-                acc[6] = __builtin_fmaf(wj, bf16_lo(v[jj].w), acc[6]);
-                acc[7] = __builtin_fmaf(wj, bf16_hi(v[jj].w), acc[7]);
+#pragma unroll
+                for (int i = 0; i < kParChunks; ++i) {
+                    acc[i][0] = __builtin_fmaf(wj, bf16_lo(v[jj][i].x), acc[i][0]);
+                    acc[i][1] = __builtin_fmaf(wj, bf16_hi(v[jj][i].x), acc[i][1]);
+                    acc[i][2] = __builtin_fmaf(wj, bf16_lo(v[jj][i].y), acc[i][2]);
+                    acc[i][3] = __builtin_fmaf(wj, bf16_hi(v[jj][i].y), acc[i][3]);
+                    acc[i][4] = __builtin_fmaf(wj, bf16_lo(v[jj][i].z), acc[i][4]);
+                    acc[i][5] = __builtin_fmaf(wj, bf16_hi(v[jj][i].z), acc[i][5]);
+                    acc[i][6] = __builtin_fmaf(wj, bf16_lo(v[jj][i].w), acc[i][6]);
+                    acc[i][7] = __builtin_fmaf(wj, bf16_hi(v[jj][i].w), acc[i][7]);
+                }
             }
         }
-        if (BF16_OUT) {
-            u32x4 o;
-            o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-            o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-            o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-            o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
-            __builtin_nontemporal_store(o, (u32x4 *)partials + r * nvec + c);
-        } else {
-            u32x4 *o = (u32x4 *)partials + (r * nvec + c) * 2;
-            const u32x4 a = {__float_as_uint(acc[0]), __float_as_uint(acc[1]),
-                             __float_as_uint(acc[2]), __float_as_uint(acc[3])};
-            const u32x4 b = {__float_as_uint(acc[4]), __float_as_uint(acc[5]),
-                             __float_as_uint(acc[6]), __float_as_uint(acc[7])};
-            __builtin_nontemporal_store(a, o);
-            __builtin_nontemporal_store(b, o + 1);
+#pragma unroll
+        for (int i = 0; i < kParChunks; ++i) {
+            const int c = c0 + i * kThreads;
+            if (c >= c_end)
+                continue;
+            if (BF16_OUT) {
+                u32x4 o;
+                o.x = f32_to_bf16(acc[i][0]) | (f32_to_bf16(acc[i][1]) << 16);
+                o.y = f32_to_bf16(acc[i][2]) | (f32_to_bf16(acc[i][3]) << 16);
+                o.z = f32_to_bf16(acc[i][4]) | (f32_to_bf16(acc[i][5]) << 16);
+                o.w = f32_to_bf16(acc[i][6]) | (f32_to_bf16(acc[i][7]) << 16);
+                __builtin_nontemporal_store(o, (u32x4 *)partials + r * nvec + c);
+            } else {
+                u32x4 *o = (u32x4 *)partials + (r * nvec + c) * 2;
+                const u32x4 a = {__float_as_uint(acc[i][0]), __float_as_uint(acc[i][1]),
+                                 __float_as_uint(acc[i][2]), __float_as_uint(acc[i][3])};
+                const u32x4 b = {__float_as_uint(acc[i][4]), __float_as_uint(acc[i][5]),
+                                 __float_as_uint(acc[i][6]), __float_as_uint(acc[i][7])};
+                __builtin_nontemporal_store(a, o);
+                __builtin_nontemporal_store(b, o + 1);
+            }
         }
     }
 }
 
-// Finish: lanes own 8 channels in each of kFinChunks 16-byte chunks of the
-// token's output row; the loads of up to kFinBatch partial rows are issued
-// before the first add (the adds then run in ascending host order).
-constexpr int kFinChunks = 2;
-constexpr int kFinBatch = 4;
+// Finish: lanes own 8 channels in each of FinShape::chunks 16-byte chunks of
+// the token's output row; the loads of up to FinShape::batch partial rows
+// are issued before the first add (the adds then run in ascending host
+// order). Measured on MI355X: 4 chunks x 2 rows for float32 partials, 2 x 4
+// for bf16 ones.
+template <bool BF16_IN>
+struct FinShape {
+    static constexpr int chunks = BF16_IN ? 2 : 4;
+    static constexpr int batch = BF16_IN ? 4 : 2;
+};
 
 template <bool BF16_IN>
 __device__ __forceinline__ void load_partial(const void *partials, int64_t r, int nvec, int c,
@@ -213,6 +238,7 @@ __global__ __launch_bounds__(kThreads) void relay_finish_kernel(
     }
     __syncthreads();
     const int n = s_n;
+    constexpr int kFinChunks = FinShape<BF16_IN>::chunks, kFinBatch = FinShape<BF16_IN>::batch;
     const int c_beg = blockIdx.y * slice;
     const int c_end = min(nvec, c_beg + slice);
     for (int c0 = c_beg + threadIdx.x; c0 < c_end; c0 += kThreads * kFinChunks) {
