@@ -44,7 +44,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(
         return;   // past the last token, or the layout saw out-of-range expert ids
     const int c_beg = blockIdx.y * slice;
     const int c_end = min(nvec, c_beg + slice);
-    if (threadIdx.x < k) {
+    if ((int)threadIdx.x < k) {
         s_row[threadIdx.x] = slot[t * k + threadIdx.x];
         s_w[threadIdx.x] = w[t * k + threadIdx.x];
     }

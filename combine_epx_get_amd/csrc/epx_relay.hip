@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void relay_partials_kernel(
         return;   // past the relay rows in use (also past the grid's last row)
     const int t = L.relay_token[r];
     const int n = fanout_list(L, k, r, t, s_dst, s_j, &s_n);
-    if (threadIdx.x < n)
+    if ((int)threadIdx.x < n)
         s_w[threadIdx.x] = w[(int64_t)t * k + s_j[threadIdx.x]];
     __syncthreads();
     const int c_beg = blockIdx.y * slice;
