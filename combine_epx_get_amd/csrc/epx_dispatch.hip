@@ -23,7 +23,7 @@
 // 16-lane group owns one 128-channel block: 8 bf16 per lane, block maximum by
 // lane shuffles), then the waves stream the codes and scales from LDS to the
 // destination rows.
-#include "epx_internal.h"
+#include "epx_device.h"
 
 namespace epx {
 namespace {
@@ -81,73 +81,6 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
             }
         }
     }
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// float32 pair -> two OCP E4M3FN codes (a in the low byte) by the packed
-// hardware conversion, which rounds to nearest even. Finite values beyond
-// +-448 are clamped first so that they saturate to +-448 (the conversion on
-// its own turns them into NaN); NaN stays a NaN code. Checked on every
-// float32 pattern against the integer definition (round the 23-bit mantissa
-// to 3 bits, rebias; below 2^-6 the codes are rint(|v| * 2^9)): identical for
-// every non-NaN input.
-__device__ __forceinline__ float clamp448(float v)
-{
-    return fabsf(v) > 448.0f ? __builtin_copysignf(448.0f, v) : v;
-}
-
-__device__ __forceinline__ uint32_t e4m3_pair(float a, float b)
-{
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false) & 0xFFFFu;
-}
-
-// x / s, correctly rounded, for a block scale s >= 2^-100 and |x| <= 448 s:
-// the refinement of the IEEE division expansion (reciprocal y refined once
-// per scale, two fma corrections per quotient) without its range scaling,
-// which these operands never need; the sign is restored for zero x. Over
-// every bf16 pair (x, amax) with |x| <= amax and s = amax / 448 >= 2^-100 it
-// gives the same E4M3 code as the IEEE quotient (its last bit can differ only
-// for quotients far below the smallest code).
-__device__ __forceinline__ float div_by_scale(float x, float s, float y)
-{
-    const float q0 = x * y;
-    const float r1 = __builtin_fmaf(-s, q0, x);
-    const float q1 = __builtin_fmaf(r1, y, q0);
-    const float r2 = __builtin_fmaf(-s, q1, x);
-    return __builtin_copysignf(__builtin_fmaf(r2, y, q1), x);
-}
-
-__device__ __forceinline__ float refined_reciprocal(float s)
-{
-    const float y0 = __builtin_amdgcn_rcpf(s);
-    return __builtin_fmaf(__builtin_fmaf(-s, y0, 1.0f), y0, y0);
-}
-
-// Four values of one block -> four codes (a in the low byte). zero: the
-// block is all zeros (scale 0), codes keep the sign of each zero.
-__device__ __forceinline__ uint32_t quantize4(float a, float b, float c, float d, float s, float y,
-                                              bool zero)
-{
-    if (zero) {
-        return ((__float_as_uint(a) >> 24) & 0x80u) | (((__float_as_uint(b) >> 24) & 0x80u) << 8) |
-               (((__float_as_uint(c) >> 24) & 0x80u) << 16) |
-               (((__float_as_uint(d) >> 24) & 0x80u) << 24);
-    }
-    float qa, qb, qc, qd;
-    if (s >= 0x1p-100f) {
-        qa = div_by_scale(a, s, y);
-        qb = div_by_scale(b, s, y);
-        qc = div_by_scale(c, s, y);
-        qd = div_by_scale(d, s, y);
-    } else {   // tiny blocks: the full IEEE division
-        qa = a / s;
-        qb = b / s;
-        qc = c / s;
-        qd = d / s;
-    }
-    return e4m3_pair(qa, qb) | (e4m3_pair(qc, qd) << 16);
 }
 
 // Slice [c_beg, c_end) of token t, in 16-byte bf16 chunks (c_beg, c_end and
@@ -256,20 +189,6 @@ __global__ void f32_to_e4m3_kernel(const float *__restrict__ in, uint8_t *__rest
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
         out[i] = (uint8_t)(e4m3_pair(in[i], 0.0f) & 0xFFu);
-}
-
-// Column slices per token, each a whole number of `align` chunks: at least
-// `target` workgroups in all (small batches need slices to cover the GPU).
-int slice_width(int T, int nvec, int align, int max_width, int target)
-{
-    int want = T >= target ? 1 : (target + T - 1) / T;
-    int width = (nvec + want - 1) / want;
-    width = ((width + align - 1) / align) * align;
-    if (width < 4 * align && nvec > 4 * align)
-        width = 4 * align;        // no slice below 4 alignment units
-    if (width > max_width)
-        width = (max_width / align) * align;
-    return width < nvec ? width : nvec;
 }
 
 }  // namespace

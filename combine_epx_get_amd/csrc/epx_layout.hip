@@ -25,67 +25,10 @@
 //   more: count, a column scan (one wave per counter), assign.
 // Every per-pair rank and host is computed once, with division constants
 // prepared on the host, and staged in LDS with the chunk's ids.
-#include "epx_internal.h"
+#include "epx_device.h"
 
 namespace epx {
 namespace {
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
-
-// DPP lane moves (gfx9): row_shr:n moves each 16-lane row's values n lanes
-// up (lanes below n in the row read 0: bound_ctrl); row_bcast:15 / 31 hand
-// lane 15 / 31 to the next row(s), written only where row_mask allows.
-constexpr int kDppRowShr = 0x110;
-constexpr int kDppRowBcast15 = 0x142;
-constexpr int kDppRowBcast31 = 0x143;
-
-template <int CTRL, int ROW_MASK = 0xf, bool BOUND_ZERO = true>
-__device__ __forceinline__ int dpp(int v)
-{
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, BOUND_ZERO);
-}
-
-// Inclusive scan within each 16-lane row.
-__device__ __forceinline__ int row_inclusive_scan(int v)
-{
-    v += dpp<kDppRowShr + 1>(v);
-    v += dpp<kDppRowShr + 2>(v);
-    v += dpp<kDppRowShr + 4>(v);
-    v += dpp<kDppRowShr + 8>(v);
-    return v;
-}
-
-__device__ __forceinline__ int wave_inclusive_scan(int v)
-{
-    v = row_inclusive_scan(v);
-    v += dpp<kDppRowBcast15, 0xa, false>(v);   // rows 1 and 3 add the end of rows 0 and 2
-    v += dpp<kDppRowBcast31, 0xc, false>(v);   // rows 2 and 3 add the end of rows 0-1
-    return v;
-}
-
-// Maximum over the wave (values >= 0), the same in every lane.
-__device__ __forceinline__ int wave_max(int v)
-{
-    v = max(v, dpp<kDppRowShr + 1>(v));
-    v = max(v, dpp<kDppRowShr + 2>(v));
-    v = max(v, dpp<kDppRowShr + 4>(v));
-    v = max(v, dpp<kDppRowShr + 8>(v));
-    v = max(v, dpp<kDppRowBcast15, 0xa, false>(v));
-    v = max(v, dpp<kDppRowBcast31, 0xc, false>(v));
-    return __builtin_amdgcn_readlane(v, kWave - 1);
-}
-
-// Lanes whose `e` equals mine among the active lanes (ballot multisplit).
-__device__ __forceinline__ uint64_t match_peers(bool active, int e, int nbits)
-{
-    uint64_t peers = __ballot(active);
-    for (int bit = 0; bit < nbits; ++bit) {
-        const bool on = (e >> bit) & 1;
-        const uint64_t m = __ballot(on);
-        peers &= on ? m : ~m;
-    }
-    return peers;
-}
 
 // Stage pairs [0, np) of a chunk: ids, their ranks and hosts (-1 for a bad id).
 __device__ __forceinline__ void stage_pairs(const int32_t *__restrict__ idx, int64_t p0, int np,
@@ -139,21 +82,6 @@ __device__ __forceinline__ void count_pair(int p, const Geometry &g, const int32
         atomicAdd(&s_rtok[r], 1);
     if (new_host)
         atomicAdd(&s_htok[h], 1);
-}
-
-// Relay rows past the used ones, [used, capacity) split over `parts`, read as empty.
-__device__ __forceinline__ void clear_relay_tail(const Geometry &g, int64_t used, int part,
-                                                 int parts, int nthreads, const epx_layout &L)
-{
-    const int64_t cap = (int64_t)g.T * min(g.k, g.H);
-    const int64_t per = (cap + parts - 1) / parts;
-    const int64_t beg = max(used, (int64_t)part * per), end = min(cap, (int64_t)(part + 1) * per);
-    for (int64_t r = beg + threadIdx.x; r < end; r += nthreads) {
-        L.relay_token[r] = -1;
-        L.fanout_rank_mask[r] = 0u;
-    }
-    for (int64_t i = beg * g.k + threadIdx.x; i < end * g.k; i += nthreads)
-        L.fanout_expert[i] = -1;
 }
 
 // Relay rows of up to 64 consecutive tokens (one per lane: token t, its
@@ -270,51 +198,6 @@ __global__ __launch_bounds__(256) void layout_scan_kernel(Geometry g, int32_t *_
     }
     if (lane == 0)
         ws[(int64_t)ncol * g.Gs + col] = carry;
-}
-
-// ---------------------------------------------------------------- expert order
-// Rows are ordered by expert in the scan order of this function: expert ids
-// ascending, or with m > 1 expert groups (per-expert overlap) by (group,
-// rank, local index in the group), so that one group's rows form one range.
-__device__ __forceinline__ int expert_at(const Geometry &g, int q)
-{
-    if (g.m == 1)
-        return q;
-    const int per_group = g.R * g.epg;
-    const int grp = q / per_group;
-    const int rem = q - grp * per_group;
-    const int r = rem / g.epg;
-    return r * g.epr + grp * g.epg + (rem - r * g.epg);
-}
-
-// First row of block b = group * R + rank (b == m * R: the total), from the
-// final expert offsets eoff[0, E].
-__device__ __forceinline__ int block_start(const Geometry &g, const int32_t *eoff, int b)
-{
-    if (b >= g.m * g.R)
-        return eoff[g.E];
-    const int grp = b / g.R, r = b - grp * g.R;
-    return eoff[r * g.epr + grp * g.epg];
-}
-
-// Per-rank and per-group offsets from the final expert offsets (threads
-// [0, nthreads) of the workgroup): rank_offset (-1 with groups: a rank's rows
-// are then split over the groups), rank_rows and group_offset.
-__device__ void write_rank_and_group_offsets(const Geometry &g, const int32_t *eoff,
-                                             const epx_layout &L, int nthreads)
-{
-    const int tid = threadIdx.x;
-    for (int r = tid; r <= g.R; r += nthreads) {
-        L.rank_offset[r] = g.m == 1 ? eoff[r * g.epr] : -1;
-        if (r < g.R) {
-            int rows = 0;
-            for (int grp = 0; grp < g.m; ++grp)
-                rows += block_start(g, eoff, grp * g.R + r + 1) - block_start(g, eoff, grp * g.R + r);
-            L.rank_rows[r] = rows;
-        }
-    }
-    for (int b = tid; b <= g.m * g.R; b += nthreads)
-        L.group_offset[b] = block_start(g, eoff, b);
 }
 
 // ---------------------------------------------------------------- assign
