@@ -84,10 +84,13 @@ def group_bytes(idx, E, R, m, hidden, fp8):
     return out
 
 
+GRAPH_STEPS = 16   # layers captured in one graph under --graph
+
 KERNEL_SOURCE = {"dispatch_bf16_kernel": "epx_dispatch.hip", "dispatch_fp8_kernel": "epx_dispatch.hip",
                  "combine_kernel": "epx_combine.hip", "relay_fanout_kernel": "epx_relay.hip",
                  "relay_partials_kernel": "epx_relay.hip", "relay_finish_kernel": "epx_relay.hip",
-                 "combine_group_kernel": "epx_combine.hip", "plan_swaps_kernel": "epx_balance.hip"}
+                 "combine_group_kernel": "epx_combine.hip", "plan_swaps_kernel": "epx_balance.hip",
+                 "layout_dispatch_kernel": "epx_fused.hip"}
 
 
 def relay_receive_bytes(T, k, H, hidden, rows, fp8, f32_partials):
@@ -108,10 +111,10 @@ def relay_receive_bytes(T, k, H, hidden, rows, fp8, f32_partials):
 
 def kernel_sources_hash(kernel: str = "") -> str:
     """Hash of the source file holding `kernel` (plus the shared internal
-    header); of every kernel source when the kernel is not listed."""
+    headers); of every kernel source when the kernel is not listed."""
     csrc = os.path.join(ROOT, "combine_epx_get_amd", "csrc")
     if kernel in KERNEL_SOURCE:
-        files = [os.path.join(csrc, KERNEL_SOURCE[kernel]), os.path.join(csrc, "epx_internal.h")]
+        files = [os.path.join(csrc, f) for f in (KERNEL_SOURCE[kernel], "epx_internal.h", "epx_device.h")]
     else:
         files = sorted(glob.glob(os.path.join(csrc, "*")))
     h = hashlib.sha256()
@@ -136,7 +139,8 @@ def load_counter_traffic(kernel: str, tag: str):
 KERNEL_NAMES = ("dispatch_bf16_kernel", "dispatch_fp8_kernel", "combine_kernel",
                 "relay_fanout_kernel", "relay_partials_kernel", "relay_finish_kernel",
                 "layout_small_kernel", "layout_count_kernel", "layout_scan_kernel",
-                "layout_assign_kernel", "combine_group_kernel", "plan_swaps_kernel")
+                "layout_assign_kernel", "combine_group_kernel", "plan_swaps_kernel",
+                "layout_dispatch_kernel")
 
 
 def ingest_counters(fetch_csv: str, write_csv: str, tag: str, command: str) -> list:
@@ -229,9 +233,12 @@ def main(argv=None) -> int:
     ap.add_argument("--groups", type=int, default=1, metavar="M",
                     help="expert groups (per-expert overlap): step = grouped layout, M group "
                          "dispatches, M group combines (per-expert mode)")
+    ap.add_argument("--fused", action="store_true",
+                    help="layout and dispatch in one call (epx_layout_dispatch: one launch for "
+                         "decode-sized batches)")
     ap.add_argument("--graph", action="store_true",
-                    help="also time the step captured once in a HIP graph and replayed (layer time "
-                         "without per-launch host overhead)")
+                    help="also time layers captured in a HIP graph (16 per graph) and replayed: the "
+                         "layer time without per-launch host overhead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -245,6 +252,8 @@ def main(argv=None) -> int:
         tag0 = f"{w0}_{args.mode or W0.WORKLOADS[w0].modes[0]}_{args.dtype or W0.WORKLOADS[w0].dtypes[0]}"
         if args.groups > 1:
             tag0 += f"_g{args.groups}"
+        if args.fused:
+            tag0 += "_fused"
         for pth in ingest_counters(*args.ingest_counters, tag0, args.ingest_command):
             print(pth)
         return 0
@@ -272,6 +281,11 @@ def main(argv=None) -> int:
     m = args.groups
     if m > 1 and relay:
         print("--groups needs per-expert mode", file=sys.stderr)
+        return 2
+    fused = args.fused
+    if fused and (m > 1 or args.swap_planner is not None):
+        print("--fused runs layout and dispatch as one call: no groups, no swap planner between them",
+              file=sys.stderr)
         return 2
     p = epx.make_problem(T, k, w.num_experts, w.num_ranks, w.num_hosts, w.my_rank,
                          epx.MODE_HOST_RELAY if relay else epx.MODE_PER_EXPERT, m)
@@ -325,8 +339,13 @@ def main(argv=None) -> int:
                 ev[i].record(stream)
 
         rec(0)
-        epx.epx_get_layout(p, idx, L, stream)
-        rec(1)
+        if fused:
+            # layout and dispatch in one call: its time is events 0 -> 1
+            epx.epx_layout_dispatch(p, idx, L, x, out_dtype, recv, scales, stream)
+            rec(1)
+        else:
+            epx.epx_get_layout(p, idx, L, stream)
+            rec(1)
         if planner:
             i = n_plans[0] % 2
             plan_out["slot_expert"] = places[1 - i]
@@ -345,7 +364,8 @@ def main(argv=None) -> int:
                 rec(7 + m + g)
             rec(3)
             return
-        epx.epx_dispatch(p, L, x, out_dtype, recv, scales, stream)
+        if not fused:
+            epx.epx_dispatch(p, L, x, out_dtype, recv, scales, stream)
         rec(2)
         if receive:
             epx.epx_relay_fanout(p, L, recv, fan, scales, fan_sc, stream)
@@ -393,19 +413,23 @@ def main(argv=None) -> int:
             step()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
+        # GRAPH_STEPS layers per graph, so that one replay's host cost is
+        # spread over many layers and the time is the GPU's
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step()
-        for _ in range(args.warmup):
+            for _ in range(GRAPH_STEPS):
+                step()
+        replays = max(1, args.steps // GRAPH_STEPS)
+        for _ in range(max(1, args.warmup // GRAPH_STEPS)):
             graph.replay()
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record()
-        for _ in range(args.steps):
+        for _ in range(replays):
             graph.replay()
         g1.record()
         torch.cuda.synchronize()
-        graph_us = g0.elapsed_time(g1) * 1e3 / args.steps
+        graph_us = g0.elapsed_time(g1) * 1e3 / (replays * GRAPH_STEPS)
 
     lay_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     plan_ms = np.array([e[1].elapsed_time(e[6]) for e in evs])
@@ -431,8 +455,12 @@ def main(argv=None) -> int:
     us_layer = float(step_ms.mean() * 1e3)
     value = layer_bytes / (ms_per_step * 1e-3) / 1e9
 
-    per_kernel = {"layout": {"us": float(lay_ms.mean() * 1e3), "bytes": nbytes["layout"]}}
-    if m == 1:
+    if fused:
+        per_kernel = {"layout_dispatch": {"us": float(lay_ms.mean() * 1e3),
+                                          "bytes": nbytes["layout"] + nbytes["dispatch"]}}
+    else:
+        per_kernel = {"layout": {"us": float(lay_ms.mean() * 1e3), "bytes": nbytes["layout"]}}
+    if m == 1 and not fused:
         per_kernel["dispatch"] = {"us": float(dis_ms.mean() * 1e3), "bytes": nbytes["dispatch"]}
     if m > 1:
         for g in range(m):
@@ -461,8 +489,9 @@ def main(argv=None) -> int:
              "combine": "combine_kernel", "relay_fanout": "relay_fanout_kernel",
              "relay_partials": "relay_partials_kernel", "relay_finish": "relay_finish_kernel",
              "dispatch_g": "dispatch_fp8_kernel" if fp8 else "dispatch_bf16_kernel",
-             "combine_g": "combine_group_kernel"}[dom.rstrip("0123456789")]
-    tag = f"{args.workload}_{mode}_{dtype}" + (f"_g{m}" if m > 1 else "")
+             "combine_g": "combine_group_kernel",
+             "layout_dispatch": "layout_dispatch_kernel"}[dom.rstrip("0123456789")]
+    tag = f"{args.workload}_{mode}_{dtype}" + (f"_g{m}" if m > 1 else "") + ("_fused" if fused else "")
     traffic = load_counter_traffic(kname, tag)
     roofline = {"bound": "hbm", "kernel": kname,
                 "achieved": round(per_kernel[dom]["GBs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -490,7 +519,8 @@ def main(argv=None) -> int:
                    "mode": mode + ("+receive" if receive else ""), "payload": dtype,
                    **({"partials": args.partials} if receive else {}),
                    **({"swap_tau": args.swap_planner} if planner else {}),
-                   **({"expert_groups": m} if m > 1 else {})},
+                   **({"expert_groups": m} if m > 1 else {}),
+                   **({"fused_layout_dispatch": True} if fused else {})},
         "us_per_layer": round(us_layer, 2),
         **({"us_per_layer_graph": round(graph_us, 2)} if graph_us is not None else {}),
         "pct_of_peak_layer": round(100 * layer_bytes / (us_layer * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),

@@ -104,6 +104,26 @@ epx_status check_layout(const Geometry &g, const epx_layout *L)
 
 epx_status from_hip(hipError_t e) { return e == hipSuccess ? EPX_OK : EPX_ERR_DEVICE; }
 
+// The dispatch arguments (T > 0 for the pointers).
+epx_status check_dispatch(const Geometry &g, const void *x, int32_t hidden, int32_t out_dtype,
+                          const void *recv, const float *recv_scales, int64_t capacity_rows)
+{
+    if (out_dtype != EPX_BF16 && out_dtype != EPX_FP8_E4M3)
+        return EPX_ERR_ARG;
+    if (hidden < 8 || hidden % 8 != 0 || (out_dtype == EPX_FP8_E4M3 && hidden % epx::kFp8Block != 0))
+        return EPX_ERR_ARG;
+    const int64_t need = g.relay ? relay_capacity(g) : (int64_t)g.T * g.k;
+    if (capacity_rows < need)
+        return EPX_ERR_CAPACITY;
+    if (g.T == 0)
+        return EPX_OK;   // nothing to move; the activation pointers are not used
+    if (!x || !recv || !aligned(x, 16) || !aligned(recv, 16))
+        return EPX_ERR_ARG;
+    if (out_dtype == EPX_FP8_E4M3 && (!recv_scales || !aligned(recv_scales, 4)))
+        return EPX_ERR_ARG;
+    return EPX_OK;
+}
+
 // group < 0: the plain call; else one group's rows (group < m).
 epx_status dispatch_impl(const epx_problem *p, const epx_layout *layout, int group, const void *x,
                          int32_t hidden, int32_t out_dtype, void *recv, float *recv_scales,
@@ -119,19 +139,10 @@ epx_status dispatch_impl(const epx_problem *p, const epx_layout *layout, int gro
         return EPX_ERR_ARG;
     if (g.m == 1)
         group = -1;   // one group is every row (relay rows included)
-    if (out_dtype != EPX_BF16 && out_dtype != EPX_FP8_E4M3)
-        return EPX_ERR_ARG;
-    if (hidden < 8 || hidden % 8 != 0 || (out_dtype == EPX_FP8_E4M3 && hidden % epx::kFp8Block != 0))
-        return EPX_ERR_ARG;
-    const int64_t need = g.relay ? relay_capacity(g) : (int64_t)g.T * g.k;
-    if (capacity_rows < need)
-        return EPX_ERR_CAPACITY;
+    if ((st = check_dispatch(g, x, hidden, out_dtype, recv, recv_scales, capacity_rows)) != EPX_OK)
+        return st;
     if (g.T == 0)
-        return EPX_OK;   // nothing to move; the activation pointers are not used
-    if (!x || !recv || !aligned(x, 16) || !aligned(recv, 16))
-        return EPX_ERR_ARG;
-    if (out_dtype == EPX_FP8_E4M3 && (!recv_scales || !aligned(recv_scales, 4)))
-        return EPX_ERR_ARG;
+        return EPX_OK;
     const hipStream_t s = (hipStream_t)stream;
     if (out_dtype == EPX_BF16)
         return from_hip(epx::launch_dispatch_bf16(g, *layout, x, hidden, recv, group, s));
@@ -223,6 +234,34 @@ epx_status epx_dispatch(const epx_problem *p, const epx_layout *layout, const vo
 {
     return dispatch_impl(p, layout, -1, x, hidden, out_dtype, recv, recv_scales, capacity_rows,
                          stream);
+}
+
+epx_status epx_layout_dispatch(const epx_problem *p, const int32_t *topk_idx,
+                               const epx_layout *layout, const void *x, int32_t hidden,
+                               int32_t out_dtype, void *recv, float *recv_scales,
+                               int64_t capacity_rows, void *stream)
+{
+    Geometry g;
+    epx_status st = make_geometry(p, &g);
+    if (st != EPX_OK)
+        return st;
+    if ((st = check_layout(g, layout)) != EPX_OK)
+        return st;
+    if (g.T > 0 && (!topk_idx || !aligned(topk_idx, 4)))
+        return EPX_ERR_ARG;
+    if ((st = check_dispatch(g, x, hidden, out_dtype, recv, recv_scales, capacity_rows)) != EPX_OK)
+        return st;
+    const hipStream_t s = (hipStream_t)stream;
+    const bool fp8 = out_dtype == EPX_FP8_E4M3;
+    hipError_t err = hipSuccess;
+    if (g.T > 0 &&
+        epx::launch_layout_dispatch(g, topk_idx, *layout, x, hidden, fp8, recv, recv_scales, s, &err))
+        return from_hip(err);
+    if ((st = from_hip(epx::launch_layout(g, topk_idx, *layout, s))) != EPX_OK || g.T == 0)
+        return st;
+    if (!fp8)
+        return from_hip(epx::launch_dispatch_bf16(g, *layout, x, hidden, recv, -1, s));
+    return from_hip(epx::launch_dispatch_fp8(g, *layout, x, hidden, recv, recv_scales, -1, s));
 }
 
 epx_status epx_dispatch_group(const epx_problem *p, const epx_layout *layout, int32_t group,

@@ -79,6 +79,11 @@ hipError_t launch_dispatch_bf16(const Geometry &g, const epx_layout &L, const vo
 hipError_t launch_dispatch_fp8(const Geometry &g, const epx_layout &L, const void *x,
                                int32_t hidden, void *recv, float *scales, int group,
                                hipStream_t stream);
+// Layout and dispatch in one launch; false (nothing launched) when the batch
+// is too large for it. *err receives the launch status otherwise.
+bool launch_layout_dispatch(const Geometry &g, const int32_t *idx, const epx_layout &L,
+                            const void *x, int32_t hidden, bool fp8, void *recv, float *scales,
+                            hipStream_t stream, hipError_t *err);
 hipError_t launch_combine(const Geometry &g, const epx_layout &L, const void *y,
                           const float *w, int32_t hidden, void *out, hipStream_t stream);
 hipError_t launch_combine_group(const Geometry &g, const epx_layout &L, int group,

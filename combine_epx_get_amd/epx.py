@@ -62,6 +62,8 @@ _lib.epx_combine_relay_partials.argtypes = [ctypes.POINTER(epx_problem), ctypes.
                                             ctypes.c_int64, _P]
 _lib.epx_combine_relay_finish.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_layout), _P,
                                           ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P]
+_lib.epx_layout_dispatch.argtypes = [ctypes.POINTER(epx_problem), _P, ctypes.POINTER(epx_layout), _P,
+                                     ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int64, _P]
 _lib.epx_dispatch_group.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_layout), ctypes.c_int32,
                                     _P, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int64, _P]
 _lib.epx_combine_group.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_layout), ctypes.c_int32,
@@ -72,7 +74,8 @@ _lib.epx_status_string.argtypes = [ctypes.c_int]
 _lib.epx_status_string.restype = ctypes.c_char_p
 for _f in ("epx_layout_sizes", "epx_get_layout", "epx_dispatch", "epx_combine", "epx_read_error",
            "epx_f32_to_e4m3", "epx_relay_fanout", "epx_combine_relay_partials",
-           "epx_combine_relay_finish", "epx_plan_swaps", "epx_dispatch_group", "epx_combine_group"):
+           "epx_combine_relay_finish", "epx_plan_swaps", "epx_dispatch_group", "epx_combine_group",
+           "epx_layout_dispatch"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.epx_abi_version.restype = ctypes.c_int32
 NARRAYS = len(LAYOUT_FIELDS)
@@ -174,6 +177,20 @@ def epx_dispatch(problem: epx_problem, layout: Layout, x: torch.Tensor, out_dtyp
     _check(_lib.epx_dispatch(ctypes.byref(problem), ctypes.byref(layout.struct), x.data_ptr(), hidden,
                              out_dtype, recv.data_ptr(), scales_ptr, recv.shape[0], _stream(stream)),
            "epx_dispatch")
+
+
+def epx_layout_dispatch(problem: epx_problem, topk_idx: torch.Tensor, layout: Layout, x: torch.Tensor,
+                        out_dtype: int, recv: torch.Tensor, recv_scales: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    """epx_get_layout then epx_dispatch, as one launch for decode-sized batches."""
+    _need(topk_idx, torch.int32, "topk_idx", 2)
+    if tuple(topk_idx.shape) != (problem.num_tokens, problem.topk):
+        raise ValueError(f"topk_idx shape {tuple(topk_idx.shape)} != (T, k)")
+    hidden, scales_ptr = _dispatch_args(problem, x, out_dtype, recv, recv_scales)
+    _check(_lib.epx_layout_dispatch(ctypes.byref(problem), topk_idx.data_ptr(), ctypes.byref(layout.struct),
+                                    x.data_ptr(), hidden, out_dtype, recv.data_ptr(), scales_ptr,
+                                    recv.shape[0], _stream(stream)),
+           "epx_layout_dispatch")
 
 
 def epx_dispatch_group(problem: epx_problem, layout: Layout, group: int, x: torch.Tensor, out_dtype: int,

@@ -11,6 +11,7 @@
  *   epx_get_layout   -- top-k routing -> counts, offsets and row positions
  *   epx_dispatch     -- token rows -> per-expert rows (Mode 1) or one row per
  *                       destination host (Mode 2 relay), bf16 or fp8
+ *   epx_layout_dispatch -- the two above in one launch for decode batches
  *   epx_combine      -- k expert outputs per token -> weighted sum, bf16
  *   epx_relay_fanout, epx_combine_relay_partials, epx_combine_relay_finish
  *                    -- the relay's receive side and its two-level combine
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-#define EPX_ABI_VERSION 2
+#define EPX_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define EPX_API __attribute__((visibility("default")))
@@ -197,6 +198,23 @@ EPX_API epx_status epx_dispatch(const epx_problem *p, const epx_layout *layout, 
 EPX_API epx_status epx_combine(const epx_problem *p, const epx_layout *layout, const void *y,
                        int64_t y_rows, const float *topk_weights, int32_t hidden, void *out,
                        void *stream);
+
+/* Layout and dispatch in one call: the same results as epx_get_layout
+ * followed by epx_dispatch on the same stream, bit for bit (every layout
+ * array, recv and recv_scales; with ids outside [0, E) only totals[3] is
+ * defined and nothing is dispatched). For the decode batches of the digest
+ * (section 1: at most 128 tokens per GPU; section 5) the layout is small
+ * enough that every dispatch workgroup recomputes the part of it that its
+ * token needs, so the two steps run as one launch with no dependency between
+ * workgroups: used when T <= 1024, T*k <= 4096, k <= 16 and E <= 512 (and
+ * the kernel's LDS fits in 60 KB); otherwise this call makes the two
+ * launches. Arguments, alignment and capacity rules are those of the two
+ * calls; the layout's workspace may go unused. Errors: those of either
+ * call, checked before anything is launched. */
+EPX_API epx_status epx_layout_dispatch(const epx_problem *p, const int32_t *topk_idx,
+                                       const epx_layout *layout, const void *x, int32_t hidden,
+                                       int32_t out_dtype, void *recv, float *recv_scales,
+                                       int64_t capacity_rows, void *stream);
 
 /* ---- Expert groups (per-expert overlap, digest section 3.3, Figure 4).
  * The problem has num_groups = m > 1; call with group = 0 .. m-1.

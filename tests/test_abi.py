@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(epx):
 
 
 def test_abi_version_and_status_strings(epx):
-    assert epx.abi_version() == 2
+    assert epx.abi_version() == 3
     for code in range(5):
         assert epx._lib.epx_status_string(code)
 

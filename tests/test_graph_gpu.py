@@ -22,19 +22,21 @@ def epx():
 
 
 CASES = [
-    # workload, relay, groups, fp8
-    ("decode_skewed", False, 1, False),
-    ("decode_skewed", True, 1, False),
-    ("tiny", True, 1, True),
-    ("tiny", False, 2, False),
-    ("decode_uniform", False, 4, True),
+    # workload, relay, groups, fp8, fused layout and dispatch
+    ("decode_skewed", False, 1, False, False),
+    ("decode_skewed", True, 1, False, False),
+    ("tiny", True, 1, True, False),
+    ("tiny", False, 2, False, False),
+    ("decode_uniform", False, 4, True, False),
+    ("decode_skewed", True, 1, True, True),
+    ("rank_heavy", False, 1, False, True),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{'relay' if c[1] else 'expert'}-m{c[2]}-{'fp8' if c[3] else 'bf16'}"
-                                             for c in CASES])
+                                             f"{'-fused' if c[4] else ''}" for c in CASES])
 def test_graph_replays_match_eager(epx, case):
-    name, relay, m, fp8 = case
+    name, relay, m, fp8, fused = case
     w = W.WORKLOADS[name]
     d = W.make_inputs(w)
     T, k, h = d["T"], w.topk, w.hidden
@@ -58,6 +60,10 @@ def test_graph_replays_match_eager(epx, case):
     dt = epx.FP8_E4M3 if fp8 else epx.BF16
 
     def step():
+        if fused:
+            epx.epx_layout_dispatch(p, idx, L, x, dt, recv, scales)
+            epx.epx_combine(p, L, y, wts, out)
+            return
         epx.epx_get_layout(p, idx, L)
         if m > 1:
             for g in range(m):
