@@ -30,6 +30,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, public specification
 COPY_BYTES = 256 << 20       # size of the calibration copy
+EVICT_BYTES = 512 << 20      # scratch read before each step under --cold
+CEILING_BYTES = 512 << 20    # device copy timed beside the peak (read + write = 1 GiB)
 
 
 def algorithmic_bytes(T, k, H, hidden, rows, relay, fp8):
@@ -192,6 +194,25 @@ def ingest_counters(fetch_csv: str, write_csv: str, tag: str, command: str) -> l
     return out
 
 
+def copy_ceiling(torch, dev, reps: int = 5) -> float:
+    """A plain device copy of CEILING_BYTES (read + write), timed with events:
+    the best of `reps` in GB/s, the copy rate this memory system reaches in
+    the same run."""
+    src = torch.ones(CEILING_BYTES // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = float("inf")
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del src, dst
+    return 2 * CEILING_BYTES / (best * 1e-3) / 1e9
+
+
 def cpu_baseline(w, d, min_seconds=12.0, max_reps=64):
     """The oracle as it stands (single-threaded C loops) on full layers of the
     same workload: layout + per-expert bf16 dispatch + combine, repeated until
@@ -239,6 +260,9 @@ def main(argv=None) -> int:
     ap.add_argument("--graph", action="store_true",
                     help="also time layers captured in a HIP graph (16 per graph) and replayed: the "
                          "layer time without per-launch host overhead")
+    ap.add_argument("--cold", action="store_true",
+                    help="read a 512 MiB scratch buffer before every step (evicts the 256 MB "
+                         "Infinity Cache and L2); per-kernel and layer times then exclude the flush")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -387,7 +411,18 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
+    # --cold: read a 512 MiB buffer before each step. Reading (not writing)
+    # leaves clean lines in the caches, so the dirty lines of the previous
+    # step are written back during the flush and none is left for the next
+    # kernel to write back inside its own time.
+    scratch = torch.ones(EVICT_BYTES // 4, dtype=torch.int32, device=dev) if args.cold else None
+
+    def flush(i):
+        if scratch is not None:
+            scratch.max()
+
+    for i in range(args.warmup):
+        flush(i)
         step()
     torch.cuda.synchronize()
     assert epx.epx_read_error(L) == 0
@@ -398,9 +433,11 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        flush(i)
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    del scratch
 
     graph_us = None
     if args.graph:
@@ -442,7 +479,9 @@ def main(argv=None) -> int:
     else:
         com_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
     step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
-    ms_per_step = wall * 1e3 / args.steps
+    # the flush is not part of the layer: under --cold the step time comes
+    # from the events around the layer, otherwise from the wall clock
+    ms_per_step = float(step_ms.mean()) if args.cold else wall * 1e3 / args.steps
 
     nbytes = algorithmic_bytes(T, k, w.num_hosts, hidden, rows, relay, fp8)
     if receive:
@@ -455,32 +494,37 @@ def main(argv=None) -> int:
     us_layer = float(step_ms.mean() * 1e3)
     value = layer_bytes / (ms_per_step * 1e-3) / 1e9
 
+    def kern(ms, nb):
+        """Event times of one kernel over the timed steps (µs): mean (the
+        roofline's figure), median, min and max."""
+        us = np.asarray(ms, dtype=np.float64) * 1e3
+        return {"us": float(us.mean()), "us_median": float(np.median(us)), "us_min": float(us.min()),
+                "us_max": float(us.max()), "bytes": nb}
+
     if fused:
-        per_kernel = {"layout_dispatch": {"us": float(lay_ms.mean() * 1e3),
-                                          "bytes": nbytes["layout"] + nbytes["dispatch"]}}
+        per_kernel = {"layout_dispatch": kern(lay_ms, nbytes["layout"] + nbytes["dispatch"])}
     else:
-        per_kernel = {"layout": {"us": float(lay_ms.mean() * 1e3), "bytes": nbytes["layout"]}}
+        per_kernel = {"layout": kern(lay_ms, nbytes["layout"])}
     if m == 1 and not fused:
-        per_kernel["dispatch"] = {"us": float(dis_ms.mean() * 1e3), "bytes": nbytes["dispatch"]}
+        per_kernel["dispatch"] = kern(dis_ms, nbytes["dispatch"])
     if m > 1:
         for g in range(m):
             d0 = 6 if g == 0 else 7 + g - 1
             c0 = 2 if g == 0 else 7 + m + g - 1
-            per_kernel[f"dispatch_g{g}"] = {"us": float(np.mean([e[d0].elapsed_time(e[7 + g]) for e in evs]) * 1e3),
-                                            "bytes": nbytes[f"dispatch_g{g}"]}
-            per_kernel[f"combine_g{g}"] = {"us": float(np.mean([e[c0].elapsed_time(e[7 + m + g]) for e in evs]) * 1e3),
-                                           "bytes": nbytes[f"combine_g{g}"]}
+            per_kernel[f"dispatch_g{g}"] = kern([e[d0].elapsed_time(e[7 + g]) for e in evs],
+                                                nbytes[f"dispatch_g{g}"])
+            per_kernel[f"combine_g{g}"] = kern([e[c0].elapsed_time(e[7 + m + g]) for e in evs],
+                                               nbytes[f"combine_g{g}"])
     if planner:
         # counts and placement in, placement, loads, pair records and flags out
         npair = H * ((R // H) // 2)
-        per_kernel["swap_planner"] = {"us": float(plan_ms.mean() * 1e3),
-                                      "bytes": 4 * (3 * E + 2 * R + 7 * npair + H)}
+        per_kernel["swap_planner"] = kern(plan_ms, 4 * (3 * E + 2 * R + 7 * npair + H))
     if receive:
-        per_kernel["relay_fanout"] = {"us": float(fan_ms.mean() * 1e3), "bytes": nbytes["relay_fanout"]}
-        per_kernel["relay_partials"] = {"us": float(par_ms.mean() * 1e3), "bytes": nbytes["relay_partials"]}
-        per_kernel["relay_finish"] = {"us": float(fin_ms.mean() * 1e3), "bytes": nbytes["relay_finish"]}
+        per_kernel["relay_fanout"] = kern(fan_ms, nbytes["relay_fanout"])
+        per_kernel["relay_partials"] = kern(par_ms, nbytes["relay_partials"])
+        per_kernel["relay_finish"] = kern(fin_ms, nbytes["relay_finish"])
     elif m == 1:
-        per_kernel["combine"] = {"us": float(com_ms.mean() * 1e3), "bytes": nbytes["combine"]}
+        per_kernel["combine"] = kern(com_ms, nbytes["combine"])
     for v in per_kernel.values():
         v["GBs"] = v["bytes"] / (v["us"] * 1e-6) / 1e9
         v["frac_peak"] = v["GBs"] / PEAK_HBM_GBS
@@ -496,7 +540,8 @@ def main(argv=None) -> int:
     roofline = {"bound": "hbm", "kernel": kname,
                 "achieved": round(per_kernel[dom]["GBs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(per_kernel[dom]["frac_peak"], 4), "traffic": traffic,
-                "algorithmic_bytes": per_kernel[dom]["bytes"]}
+                "algorithmic_bytes": per_kernel[dom]["bytes"],
+                "copy_ceiling_GBs": round(copy_ceiling(torch, dev), 1)}
 
     cpu = None
     if args.cpu_seconds > 0 and not relay and not fp8:
@@ -521,6 +566,7 @@ def main(argv=None) -> int:
                    **({"swap_tau": args.swap_planner} if planner else {}),
                    **({"expert_groups": m} if m > 1 else {}),
                    **({"fused_layout_dispatch": True} if fused else {})},
+        "cache": "cold (512 MiB scratch read before each step)" if args.cold else "warm (back-to-back steps)",
         "us_per_layer": round(us_layer, 2),
         **({"us_per_layer_graph": round(graph_us, 2)} if graph_us is not None else {}),
         "pct_of_peak_layer": round(100 * layer_bytes / (us_layer * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),

@@ -74,5 +74,30 @@ def test_bench_prints_one_json_line():
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    assert 0 < r["copy_ceiling_GBs"] < 2 * r["peak"]
+    assert d["cache"].startswith("warm")
+    for v in d["kernels"].values():
+        assert v["us_min"] <= v["us_median"] <= v["us_max"] and v["us_min"] <= v["us"] <= v["us_max"]
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["cores"] == 1 and c["value"] > 0
+
+
+@pytest.mark.gpu
+def test_bench_cold_cache_and_fused_lines():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a visible GPU")
+    for extra in (["--cold"], ["--fused", "--graph"]):
+        buf = io.StringIO()
+        with redirect_stdout(buf):
+            rc = bench.main(["--workload", "tiny", "--mode", "relay", "--steps", "16", "--warmup", "2",
+                             "--cpu-seconds", "0", *extra])
+        assert rc == 0
+        d = json.loads(buf.getvalue().strip().splitlines()[-1])
+        if "--cold" in extra:
+            assert d["cache"].startswith("cold")
+            # under --cold the step time is the layer's event time
+            assert abs(d["ms_per_step"] * 1e3 - d["us_per_layer"]) < 0.02 * d["us_per_layer"] + 0.01
+        else:
+            assert "layout_dispatch" in d["kernels"] and d["us_per_layer_graph"] > 0
+            assert d["config"]["fused_layout_dispatch"] is True
