@@ -10,7 +10,9 @@
 //   relay_fanout:   relay row r -> per-expert rows slot[t, j] of every j with
 //                   fanout_expert[r, j] >= 0 (bf16 rows, or fp8 codes +
 //                   scales); one workgroup reads the row once and its waves
-//                   stream whole destination rows.
+//                   stream whole destination rows, 16 KiB per wave in flight
+//                   (the relay rows come from HBM: 4 KiB bursts measured
+//                   125.5 us at 4096 x 7168 bf16, 16 KiB 121.3 us).
 //   relay_partials: relay row r = (t, h) -> partial[r] = sum over those j,
 //                   ascending, of w[t, j] * y[slot[t, j]] in fp32 fma from +0,
 //                   stored as fp32 or rounded to bf16 (the return wire form).
@@ -27,7 +29,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kBurst = 4;
+constexpr int kBurst = 16;   // fan-out: row vectors per lane loaded before its stores
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
