@@ -213,21 +213,23 @@ def copy_ceiling(torch, dev, reps: int = 5) -> float:
     return 2 * CEILING_BYTES / (best * 1e-3) / 1e9
 
 
-def cpu_baseline(w, d, min_seconds=12.0, max_reps=64):
+def cpu_baseline(w, d, y_bits, relay=False, fp8=False, min_seconds=12.0, max_reps=64):
     """The oracle as it stands (single-threaded C loops) on full layers of the
-    same workload: layout + per-expert bf16 dispatch + combine, repeated until
-    about min_seconds of CPU time have been spent. Returns (seconds per
-    layer, layers timed)."""
+    same workload: layout + dispatch (per-expert or relay, bf16 or fp8) +
+    combine of the same expert outputs the GPU combines, repeated until about
+    min_seconds of CPU time have been spent. Returns (seconds per layer,
+    layers timed)."""
     import oracle
     T, k = d["topk_idx"].shape
-    y_np = None
     reps, t_total = 0, 0.0
     while reps < max_reps and (t_total < min_seconds or reps < 2):
         t0 = time.perf_counter()
-        lay = oracle.layout(d["topk_idx"], w.num_experts, w.num_ranks, w.num_hosts, w.my_rank)
-        recv = oracle.dispatch_bf16(d["x"], lay, k, w.num_hosts, False)
-        y_np = recv if y_np is None else y_np
-        oracle.combine(y_np, lay, d["topk_weights"])
+        lay = oracle.layout(d["topk_idx"], w.num_experts, w.num_ranks, w.num_hosts, w.my_rank, relay=relay)
+        if fp8:
+            oracle.dispatch_fp8(d["x"], lay, k, w.num_hosts, relay)
+        else:
+            oracle.dispatch_bf16(d["x"], lay, k, w.num_hosts, relay)
+        oracle.combine(y_bits, lay, d["topk_weights"])
         t_total += time.perf_counter() - t0
         reps += 1
     return t_total / reps, reps
@@ -324,7 +326,8 @@ def main(argv=None) -> int:
     else:
         recv = torch.empty((cap, hidden), dtype=torch.bfloat16, device=dev)
         scales = None
-    y = torch.from_numpy(W.random_bf16((T * k, hidden), seed=1000 + w.seed).view(np.int16)).view(torch.bfloat16).to(dev)
+    y_np = W.random_bf16((T * k, hidden), seed=1000 + w.seed)   # stand-in expert outputs
+    y = torch.from_numpy(y_np.view(np.int16)).view(torch.bfloat16).to(dev)
     out = torch.empty((T, hidden), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
     out_dtype = epx.FP8_E4M3 if fp8 else epx.BF16
@@ -544,12 +547,12 @@ def main(argv=None) -> int:
                 "copy_ceiling_GBs": round(copy_ceiling(torch, dev), 1)}
 
     cpu = None
-    if args.cpu_seconds > 0 and not relay and not fp8:
-        cpu_s, reps = cpu_baseline(w, d, args.cpu_seconds)
+    if args.cpu_seconds > 0 and not receive and m == 1:
+        cpu_s, reps = cpu_baseline(w, d, y_np, relay, fp8, args.cpu_seconds)
         cpu = {"value": round(layer_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "us_per_layer": round(cpu_s * 1e6, 1),
-               "sample": f"{reps} full layers (layout + per-expert bf16 dispatch + combine) of the "
-                         f"{args.workload} workload, single-threaded C oracle"}
+               "sample": f"{reps} full layers (layout + {mode.replace('_', '-')} {dtype} dispatch + combine) "
+                         f"of the {args.workload} workload, single-threaded C oracle"}
 
     line = {
         "metric": "dispatch+combine µs/layer and HBM GB/s (% of MI355X peak) at 4096 tok, h=7168",
