@@ -195,6 +195,34 @@ def test_group_entry_host_checks(epx):
     assert lib.epx_get_layout(by(p), A, by(epx.epx_layout(*ptrs)), None) == 1
 
 
+def test_fused_entry_host_checks(epx):
+    """epx_layout_dispatch fails the checks of either call before launching."""
+    lib = epx._lib
+    by = ctypes.byref
+    A = 0x200000
+    p = epx.make_problem(64, 2, 16, 4, 2, 0, epx.MODE_PER_EXPERT)
+    pr = epx.make_problem(64, 2, 16, 4, 2, 0, epx.MODE_HOST_RELAY)
+    L = _fake_layout(epx, relay=False)
+    # layout side: routing ids missing or misaligned, relay arrays missing, no layout
+    assert lib.epx_layout_dispatch(by(p), None, by(L), A, 256, 0, A, None, 128, None) == 1
+    assert lib.epx_layout_dispatch(by(p), A + 2, by(L), A, 256, 0, A, None, 128, None) == 1
+    assert lib.epx_layout_dispatch(by(pr), A, by(L), A, 256, 0, A, None, 128, None) == 1
+    assert lib.epx_layout_dispatch(by(p), A, None, A, 256, 0, A, None, 128, None) == 1
+    # dispatch side: dtype, hidden, alignment, fp8 scales, capacity
+    assert lib.epx_layout_dispatch(by(p), A, by(L), A, 256, 5, A, None, 128, None) == 1
+    assert lib.epx_layout_dispatch(by(p), A, by(L), A, 252, 0, A, None, 128, None) == 1
+    assert lib.epx_layout_dispatch(by(p), A, by(L), A, 264, 1, A, A, 128, None) == 1
+    assert lib.epx_layout_dispatch(by(p), A, by(L), A + 8, 256, 0, A, None, 128, None) == 1
+    assert lib.epx_layout_dispatch(by(p), A, by(L), A, 256, 0, A + 4, None, 128, None) == 1
+    assert lib.epx_layout_dispatch(by(p), A, by(L), A, 256, 1, A, None, 128, None) == 1
+    assert lib.epx_layout_dispatch(by(p), A, by(L), A, 256, 0, A, None, 127, None) == 3
+    LR = _fake_layout(epx, relay=True)
+    assert lib.epx_layout_dispatch(by(pr), A, by(LR), A, 256, 0, A, None, 127, None) == 3
+    # geometry
+    bad = epx.make_problem(64, 2, 16, 3, 1, 0, epx.MODE_PER_EXPERT)   # E % R != 0
+    assert lib.epx_layout_dispatch(by(bad), A, by(L), A, 256, 0, A, None, 128, None) == 1
+
+
 def test_binding_rejects_wrong_tensors(epx):
     import torch
     p = epx.make_problem(4, 2, 16, 4, 2)
