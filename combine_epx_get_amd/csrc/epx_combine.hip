@@ -13,25 +13,13 @@
 // issues the loads of up to 8 expert rows for all its chunks before the
 // first fma (up to 16 x 16 bytes in flight per lane).
 // Reads T*k*h*2 bytes and writes T*h*2: an HBM-bound gather.
-#include "epx_internal.h"
+#include "epx_device.h"
 
 namespace epx {
 namespace {
 
 constexpr int kBatch = 8;    // expert rows loaded before the fmas
 constexpr int kChunks = 2;   // 16-byte chunks per lane (group combine)
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// float32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return ((u >> 16) & 0x8000u) | 0x7FC0u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 
 template <int CHUNKS>
 __global__ __launch_bounds__(1024) void combine_kernel(

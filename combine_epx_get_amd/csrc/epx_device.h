@@ -1,5 +1,5 @@
-// epx_device.h -- device helpers shared by the layout, dispatch and fused
-// layout-and-dispatch kernels (internal; not part of the C ABI).
+// epx_device.h -- device helpers shared by the kernels of libepx (internal;
+// not part of the C ABI).
 #pragma once
 
 #include "epx_internal.h"
@@ -123,9 +123,18 @@ __device__ __forceinline__ void clear_relay_tail(const Geometry &g, int64_t used
         L.fanout_expert[i] = -1;
 }
 
-// ---------------------------------------------------------------- fp8
+// ---------------------------------------------------------------- bf16 and fp8
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return ((u >> 16) & 0x8000u) | 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 
 // float32 pair -> two OCP E4M3FN codes (a in the low byte) by the packed
 // hardware conversion, which rounds to nearest even. Finite values beyond

@@ -22,7 +22,7 @@
 // All three are HBM-bound gathers/scatters like dispatch and combine. Relay
 // rows are visited up to the row capacity; workgroups past totals[1] (the
 // rows in use) return at once.
-#include "epx_internal.h"
+#include "epx_device.h"
 
 namespace epx {
 namespace {
@@ -30,17 +30,6 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kBurst = 16;   // fan-out: row vectors per lane loaded before its stores
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-__device__ __forceinline__ uint32_t f32_to_bf16(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return ((u >> 16) & 0x8000u) | 0x7FC0u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 
 // The fan-out list of relay row r in ascending j: (destination slot, j).
 // Returns its length; s_dst / s_j hold up to k entries. Every thread calls it.
