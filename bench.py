@@ -262,6 +262,8 @@ def main(argv=None) -> int:
     ap.add_argument("--graph", action="store_true",
                     help="also time layers captured in a HIP graph (16 per graph) and replayed: the "
                          "layer time without per-launch host overhead")
+    ap.add_argument("--event-every", type=int, default=4, metavar="N",
+                    help="record the per-kernel HIP events on every N-th timed step (1: all)")
     ap.add_argument("--cold", action="store_true",
                     help="read a 512 MiB scratch buffer before every step (evicts the 256 MB "
                          "Infinity Cache and L2); per-kernel and layer times then exclude the flush")
@@ -432,12 +434,19 @@ def main(argv=None) -> int:
     totals = L["totals"].cpu().numpy()
     rows = int(totals[1] if relay else totals[0])
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7 + 2 * m)] for _ in range(args.steps)]
+    # Per-kernel events on every step would slow the step they measure (each
+    # record is a marker the stream waits for: about 17 µs per large-batch
+    # step), so they are recorded on the last step of every `event_every`
+    # timed steps only (never on the first, which starts on an idle queue);
+    # the other steps run as a caller would run them.
+    every = max(1, min(args.event_every, args.steps))
+    timed = [i for i in range(args.steps) if i % every == every - 1]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7 + 2 * m)] for _ in timed]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         flush(i)
-        step(evs[i])
+        step(evs[i // every] if i % every == every - 1 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     del scratch
@@ -570,6 +579,7 @@ def main(argv=None) -> int:
                    **({"expert_groups": m} if m > 1 else {}),
                    **({"fused_layout_dispatch": True} if fused else {})},
         "cache": "cold (512 MiB scratch read before each step)" if args.cold else "warm (back-to-back steps)",
+        "event_every": every,
         "us_per_layer": round(us_layer, 2),
         **({"us_per_layer_graph": round(graph_us, 2)} if graph_us is not None else {}),
         "pct_of_peak_layer": round(100 * layer_bytes / (us_layer * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
