@@ -1,8 +1,9 @@
-"""A HIP graph capturing layout, dispatch and combine replays to the eager
-results: several replays, with eager work and a synchronisation between
-them, each checked bit for bit (layout slots, dispatched rows, combined
-output). The library records no memset; every array it writes is written by
-its kernels."""
+"""A HIP graph capturing layout, dispatch and combine (or the relay receive
+side: fan-out, partials and finish) replays to the eager results: several
+replays, with eager work and a synchronisation between them, each checked
+bit for bit (layout slots, dispatched rows, fanned-out rows and partials,
+combined output). The library records no memset; every array it writes is
+written by its kernels."""
 import numpy as np
 import pytest
 import torch
@@ -22,21 +23,24 @@ def epx():
 
 
 CASES = [
-    # workload, relay, groups, fp8, fused layout and dispatch
-    ("decode_skewed", False, 1, False, False),
-    ("decode_skewed", True, 1, False, False),
-    ("tiny", True, 1, True, False),
-    ("tiny", False, 2, False, False),
-    ("decode_uniform", False, 4, True, False),
-    ("decode_skewed", True, 1, True, True),
-    ("rank_heavy", False, 1, False, True),
+    # workload, relay, groups, fp8, fused layout and dispatch, relay receive side
+    ("decode_skewed", False, 1, False, False, False),
+    ("decode_skewed", True, 1, False, False, False),
+    ("tiny", True, 1, True, False, False),
+    ("tiny", False, 2, False, False, False),
+    ("decode_uniform", False, 4, True, False, False),
+    ("decode_skewed", True, 1, True, True, False),
+    ("rank_heavy", False, 1, False, True, False),
+    ("decode_skewed", True, 1, True, False, True),
+    ("rank_light", True, 1, False, True, True),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{'relay' if c[1] else 'expert'}-m{c[2]}-{'fp8' if c[3] else 'bf16'}"
-                                             f"{'-fused' if c[4] else ''}" for c in CASES])
+                                             f"{'-fused' if c[4] else ''}{'-receive' if c[5] else ''}"
+                                             for c in CASES])
 def test_graph_replays_match_eager(epx, case):
-    name, relay, m, fp8, fused = case
+    name, relay, m, fp8, fused, receive = case
     w = W.WORKLOADS[name]
     d = W.make_inputs(w)
     T, k, h = d["T"], w.topk, w.hidden
@@ -58,11 +62,28 @@ def test_graph_replays_match_eager(epx, case):
     out = torch.empty((T, h), dtype=torch.bfloat16, device="cuda")
     carry = torch.empty((T, h), dtype=torch.float32, device="cuda") if m > 1 else None
     dt = epx.FP8_E4M3 if fp8 else epx.BF16
+    if receive:   # the relay GPU's per-expert rows and the float32 partials
+        fan = torch.empty((T * k, h), dtype=recv.dtype, device="cuda")
+        fan_sc = torch.empty((T * k, h // 128), dtype=torch.float32, device="cuda") if fp8 else None
+        part = torch.empty((cap, h), dtype=torch.float32, device="cuda")
+
+    def receive_side():
+        epx.epx_relay_fanout(p, L, recv, fan, scales, fan_sc)
+        epx.epx_combine_relay_partials(p, L, y, wts, part)
+        epx.epx_combine_relay_finish(p, L, part, out)
 
     def step():
         if fused:
             epx.epx_layout_dispatch(p, idx, L, x, dt, recv, scales)
-            epx.epx_combine(p, L, y, wts, out)
+            if receive:
+                receive_side()
+            else:
+                epx.epx_combine(p, L, y, wts, out)
+            return
+        if receive:
+            epx.epx_get_layout(p, idx, L)
+            epx.epx_dispatch(p, L, x, dt, recv, scales)
+            receive_side()
             return
         epx.epx_get_layout(p, idx, L)
         if m > 1:
@@ -81,6 +102,11 @@ def test_graph_replays_match_eager(epx, case):
         if scales is not None:
             scales.fill_(-1.0)
         out.view(torch.int16).fill_(SENTINEL_BF16)
+        if receive:
+            fan.view(torch.uint8).fill_(SENTINEL_U8)
+            if fan_sc is not None:
+                fan_sc.fill_(-1.0)
+            part.fill_(float("nan"))
 
     def snapshot():
         torch.cuda.synchronize()
@@ -89,6 +115,11 @@ def test_graph_replays_match_eager(epx, case):
                 "recv": recv.view(torch.uint8)[:rows].cpu().numpy().copy(), "out": _bits(out).copy()}
         if scales is not None:
             snap["scales"] = scales[:rows].cpu().numpy().copy()
+        if receive:
+            snap["fan"] = fan.view(torch.uint8).cpu().numpy().copy()
+            snap["part"] = part[:rows].cpu().numpy().copy()
+            if fan_sc is not None:
+                snap["fan_sc"] = fan_sc.cpu().numpy().copy()
         return snap
 
     clear()
