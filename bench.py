@@ -259,9 +259,10 @@ def main(argv=None) -> int:
     ap.add_argument("--fused", action="store_true",
                     help="layout and dispatch in one call (epx_layout_dispatch: one launch for "
                          "decode-sized batches)")
-    ap.add_argument("--graph", action="store_true",
+    ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=None,
                     help="also time layers captured in a HIP graph (16 per graph) and replayed: the "
-                         "layer time without per-launch host overhead")
+                         "layer time without per-launch host overhead (default: on, except with "
+                         "--swap-planner)")
     ap.add_argument("--event-every", type=int, default=4, metavar="N",
                     help="record the per-kernel HIP events on every N-th timed step (1: all)")
     ap.add_argument("--cold", action="store_true",
@@ -452,10 +453,10 @@ def main(argv=None) -> int:
     del scratch
 
     graph_us = None
-    if args.graph:
-        if planner:
-            print("--graph does not capture the swap planner's alternating placement", file=sys.stderr)
-            return 2
+    if args.graph and planner:
+        print("--graph does not capture the swap planner's alternating placement", file=sys.stderr)
+        return 2
+    if args.graph if args.graph is not None else not planner:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
