@@ -171,7 +171,9 @@ SHAPES = [
     (5000, 8, 256, 256, 64, 200, 128, "uniform"),  # 64 hosts, 1 expert per rank
     (200, 32, 64, 8, 4, 2, 136, "zipf"),        # k > 16 in the multi-workgroup layout (32-token chunks)
     (100, 64, 128, 16, 8, 3, 128, "uniform"),   # k = 64 there: 16-token chunks, assign sums columns
-    (1500, 24, 96, 12, 3, 7, 128, "zipf"),      # k = 24: 42-token chunks, 36 workgroups, scan kernel
+    (1500, 24, 96, 12, 3, 7, 128, "zipf"),      # k = 24: 42-token chunks, 36 workgroups
+    (8200, 8, 256, 32, 4, 5, 128, "zipf"),      # 65 600 pairs: 257 chunk workgroups, a ragged last chunk
+    (8192, 8, 256, 16, 2, 3, 128, "uniform"),   # 65 536 pairs: 256 full chunks
 ]
 
 
