@@ -92,7 +92,7 @@ KERNEL_SOURCE = {"dispatch_bf16_kernel": "epx_dispatch.hip", "dispatch_fp8_kerne
                  "combine_kernel": "epx_combine.hip", "relay_fanout_kernel": "epx_relay.hip",
                  "relay_partials_kernel": "epx_relay.hip", "relay_finish_kernel": "epx_relay.hip",
                  "combine_group_kernel": "epx_combine.hip", "plan_swaps_kernel": "epx_balance.hip",
-                 "layout_dispatch_kernel": "epx_fused.hip"}
+                 "layout_dispatch_kernel": "epx_fused.hip", "assign_copy_bf16_kernel": "epx_layout.hip"}
 
 
 def relay_receive_bytes(T, k, H, hidden, rows, fp8, f32_partials):
@@ -125,6 +125,17 @@ def kernel_sources_hash(kernel: str = "") -> str:
     return h.hexdigest()[:16]
 
 
+def fused_kernel(T, k, E, relay, fp8):
+    """The kernel that copies the rows in an epx_layout_dispatch call: the
+    single-launch kernel at decode sizes, the assign-and-copy launch for
+    larger per-expert bf16 batches, else the plain dispatch kernel."""
+    if T <= 1024 and T * k <= 4096 and k <= 16 and E <= 512:
+        return "layout_dispatch_kernel"
+    if not relay and not fp8 and k <= 16:
+        return "assign_copy_bf16_kernel"
+    return "dispatch_fp8_kernel" if fp8 else "dispatch_bf16_kernel"
+
+
 def load_counter_traffic(kernel: str, tag: str):
     """HBM traffic per launch from a committed rocprofv3 counter summary for
     this kernel and workload tag (workload_mode_payload), if it was taken on
@@ -142,7 +153,7 @@ KERNEL_NAMES = ("dispatch_bf16_kernel", "dispatch_fp8_kernel", "combine_kernel",
                 "relay_fanout_kernel", "relay_partials_kernel", "relay_finish_kernel",
                 "layout_small_kernel", "layout_count_kernel", "layout_scan_kernel",
                 "layout_assign_kernel", "combine_group_kernel", "plan_swaps_kernel",
-                "layout_dispatch_kernel")
+                "layout_dispatch_kernel", "assign_copy_bf16_kernel")
 
 
 def ingest_counters(fetch_csv: str, write_csv: str, tag: str, command: str) -> list:
@@ -547,7 +558,7 @@ def main(argv=None) -> int:
              "relay_partials": "relay_partials_kernel", "relay_finish": "relay_finish_kernel",
              "dispatch_g": "dispatch_fp8_kernel" if fp8 else "dispatch_bf16_kernel",
              "combine_g": "combine_group_kernel",
-             "layout_dispatch": "layout_dispatch_kernel"}[dom.rstrip("0123456789")]
+             "layout_dispatch": fused_kernel(T, k, w.num_experts, relay, fp8)}[dom.rstrip("0123456789")]
     tag = f"{args.workload}_{mode}_{dtype}" + (f"_g{m}" if m > 1 else "") + ("_fused" if fused else "")
     traffic = load_counter_traffic(kname, tag)
     roofline = {"bound": "hbm", "kernel": kname,

@@ -202,7 +202,6 @@ __global__ __launch_bounds__(256) void layout_scan_kernel(Geometry g, int32_t *_
 
 // ---------------------------------------------------------------- assign
 constexpr int kAssignThreads = 512;
-constexpr int kAssignWaves = kAssignThreads / kWave;
 // Up to this many workgroups the assign kernel sums the count columns itself
 // (no scan launch); measured on MI355X, 64 workgroups summing 64-entry
 // columns cost more than the scan launch they save.
@@ -210,11 +209,12 @@ constexpr int kSumsMaxG = 16;
 
 // Exclusive scan of the expert counts src[0, E) (LDS, by expert id) in the
 // row order of expert_at into dst[0, E] (LDS, by expert id), dst[E] = total.
+template <int NT>
 __device__ void block_exclusive_scan(const Geometry &g, const int32_t *src, int32_t *dst,
                                      int32_t *s_wsum)
 {
     const int tid = threadIdx.x, n = g.E, wave = tid / kWave;
-    const int per = (n + kAssignThreads - 1) / kAssignThreads;
+    const int per = (n + NT - 1) / NT;
     const int beg = min(tid * per, n), end = min(beg + per, n);
     int sum = 0;
     for (int i = beg; i < end; ++i)
@@ -232,7 +232,7 @@ __device__ void block_exclusive_scan(const Geometry &g, const int32_t *src, int3
         dst[e] = run;
         run += v;
     }
-    if (tid == kAssignThreads - 1)
+    if (tid == NT - 1)
         dst[n] = run;
 }
 
@@ -245,12 +245,11 @@ __device__ void block_exclusive_scan(const Geometry &g, const int32_t *src, int3
 // of them counts its pairs per expert, a scan over these waves gives each its
 // first row per expert, and they then assign their rows at once. Relay rows
 // are assigned host by host, one host per wave.
-template <bool SUMS>
-__global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
-    const int32_t *__restrict__ idx, Geometry g, const int32_t *__restrict__ ws, epx_layout L,
-    int nww)
+template <bool SUMS, int NT>
+__device__ void assign_chunk(const int32_t *__restrict__ idx, const Geometry &g,
+                             const int32_t *__restrict__ ws, const epx_layout &L, int nww, int b,
+                             int32_t *lds)
 {
-    extern __shared__ __align__(16) int32_t lds[];
     const int ncol = g.E + g.R + g.H + 1;
     const int kc = g.ct * g.k;
     const int cs = g.E + 1;                // padded per-wave stride (distinct LDS banks)
@@ -263,23 +262,23 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
     int32_t *s_rk = s_idx + kc;
     int32_t *s_hk = s_rk + kc;
     int32_t *s_wc = s_hk + kc;             // [nww][cs] per-wave counts, then wave bases
-    __shared__ int32_t s_wsum[kAssignWaves];
-    __shared__ int32_t s_wmax[kAssignWaves];
+    __shared__ int32_t s_wsum[(NT / kWave)];
+    __shared__ int32_t s_wmax[(NT / kWave)];
 
-    const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int t0 = b * g.ct;
     const int nt = max(0, min(g.ct, g.T - t0));
     const int np = nt * g.k;
     const int64_t p0 = (int64_t)t0 * g.k;
     const uint64_t below = (1ull << lane) - 1ull;
 
-    stage_pairs(idx, p0, np, g, s_idx, s_rk, s_hk, kAssignThreads);
-    for (int i = tid; i < nww * cs; i += kAssignThreads)
+    stage_pairs(idx, p0, np, g, s_idx, s_rk, s_hk, NT);
+    for (int i = tid; i < nww * cs; i += NT)
         s_wc[i] = 0;
     if (SUMS) {
         // each thread sums whole columns as 16-byte vectors (Gs % 4 == 0;
         // entries [G, Gs) are padding, never written)
-        for (int c = tid; c < ncol; c += kAssignThreads) {
+        for (int c = tid; c < ncol; c += NT) {
             const int4 *col = (const int4 *)(ws + (int64_t)c * g.Gs);
             int tot = 0, pre = 0;
             for (int i = 0; 4 * i < g.Gs; ++i) {
@@ -294,7 +293,7 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
             s_pre[c] = pre;
         }
     } else {
-        for (int c = tid; c < ncol; c += kAssignThreads) {
+        for (int c = tid; c < ncol; c += NT) {
             s_tot[c] = ws[(int64_t)ncol * g.Gs + c];
             s_pre[c] = ws[(int64_t)c * g.Gs + b];
         }
@@ -320,8 +319,8 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
             s_wc[wave * cs + e] += __popcll(peers);
     }
     if (g.relay)
-        token_host_masks(nt, g, s_hk, s_hmask, kAssignThreads);
-    block_exclusive_scan(g, s_tot, s_eoff, s_wsum);   // synchronises the workgroup
+        token_host_masks(nt, g, s_hk, s_hmask, NT);
+    block_exclusive_scan<NT>(g, s_tot, s_eoff, s_wsum);   // synchronises the workgroup
     if (wave == 0) {
         const int v = lane < g.H ? s_tot[g.E + g.R + lane] : 0;
         const int incl = wave_inclusive_scan(v);
@@ -332,7 +331,7 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
     }
     // each wave's first row per expert: the expert's offset, the rows of
     // earlier workgroups, then those of earlier waves
-    for (int e = tid; e < g.E; e += kAssignThreads) {
+    for (int e = tid; e < g.E; e += NT) {
         int run = s_pre[e];
         for (int w = 0; w < nww; ++w) {
             const int v = s_wc[w * cs + e];
@@ -343,15 +342,15 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
     __syncthreads();
 
     if (b == 0) {
-        for (int e = tid; e <= g.E; e += kAssignThreads) {
+        for (int e = tid; e <= g.E; e += NT) {
             L.expert_offset[e] = s_eoff[e];
             if (e < g.E)
                 L.expert_count[e] = s_tot[e];
         }
-        write_rank_and_group_offsets(g, s_eoff, L, kAssignThreads);
-        for (int r = tid; r < g.R; r += kAssignThreads)
+        write_rank_and_group_offsets(g, s_eoff, L, NT);
+        for (int r = tid; r < g.R; r += NT)
             L.rank_tokens[r] = s_tot[g.E + r];
-        for (int h = tid; h <= g.H; h += kAssignThreads) {
+        for (int h = tid; h <= g.H; h += NT) {
             L.host_offset[h] = s_hoff[h];
             if (h < g.H) {
                 L.host_tokens[h] = s_tot[g.E + g.R + h];
@@ -359,7 +358,7 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
             }
         }
         int m = 0;
-        for (int e = tid; e < g.E; e += kAssignThreads)
+        for (int e = tid; e < g.E; e += NT)
             m = max(m, s_tot[e]);
         m = wave_max(m);
         if (lane == 0)
@@ -367,7 +366,7 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
         __syncthreads();
         if (tid == 0) {
             int mm = 0;
-            for (int w = 0; w < kAssignWaves; ++w)
+            for (int w = 0; w < (NT / kWave); ++w)
                 mm = max(mm, s_wmax[w]);
             L.totals[0] = g.T * g.k;
             L.totals[1] = s_hoff[g.H];
@@ -394,10 +393,118 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
     }
     if (!g.relay)
         return;
-    for (int h = wave; h < g.H; h += kAssignWaves)
+    for (int h = wave; h < g.H; h += (NT / kWave))
         relay_item(lane < nt, t0 + lane, lane, h, g, s_idx, s_hk, s_rk, s_hmask,
                    s_hoff[h] + s_pre[g.E + g.R + h], L);
-    clear_relay_tail(g, s_hoff[g.H], b, g.G, kAssignThreads, L);
+    clear_relay_tail(g, s_hoff[g.H], b, g.G, NT, L);
+}
+
+template <bool SUMS>
+__global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
+    const int32_t *__restrict__ idx, Geometry g, const int32_t *__restrict__ ws, epx_layout L,
+    int nww)
+{
+    extern __shared__ __align__(16) int32_t lds[];
+    assign_chunk<SUMS, kAssignThreads>(idx, g, ws, L, nww, blockIdx.x, lds);
+}
+
+// ---------------------------------------------------------------- assign + dispatch
+// Per-expert bf16 batches past the single-launch decode path: after the
+// count and scan launches, one launch both assigns the rows (items [0, G):
+// the chunk workgroups of the assign kernel, unchanged) and copies the
+// tokens (item G + t), so that no copy waits for an assign launch to end.
+// A token workgroup reads nothing the assign workgroups write: the row of
+// its pair (t, j) with expert e is the rows of the experts before e (an
+// exclusive scan of the column totals), plus the rows of e in earlier chunks
+// (the scan's prefix for t's chunk), plus the pairs of t's chunk before
+// (t, j) with expert e -- the assign kernel's row, bit for bit.
+constexpr int kFusedThreads = 256;
+constexpr int kFusedWaves = kFusedThreads / kWave;
+constexpr int kFusedBurst = 16;   // 16-byte chunks per lane per burst
+constexpr int kFusedMaxK = 16;
+
+__global__ __launch_bounds__(kFusedThreads) void assign_copy_bf16_kernel(
+    const int32_t *__restrict__ idx, Geometry g, const int32_t *__restrict__ ws, epx_layout L,
+    int nww, const u32x4 *__restrict__ x, int nvec, int slice, u32x4 *__restrict__ recv)
+{
+    extern __shared__ __align__(16) int32_t lds[];
+    __shared__ int32_t s_e[kFusedMaxK];
+    __shared__ int32_t s_pre[kFusedMaxK];
+    __shared__ int32_t s_cnt[kFusedMaxK];
+    __shared__ int32_t s_rows[kFusedMaxK];
+    __shared__ int32_t s_wsum[kFusedWaves];
+    const int64_t item = item_index();
+    if (item < g.G) {
+        if (blockIdx.y == 0)
+            assign_chunk<false, kFusedThreads>(idx, g, ws, L, nww, (int)item, lds);
+        return;
+    }
+    const int64_t t = item - g.G;
+    if (t >= g.T)
+        return;
+    const int ncol = g.E + g.R + g.H + 1;
+    const int32_t *tot = ws + (int64_t)ncol * g.Gs;   // column totals
+    if (tot[ncol - 1] != 0)
+        return;   // out-of-range ids: the assign workgroups report them, nothing moves
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int c = (int)(t / g.ct);
+    int32_t *s_tot = lds;           // [E] rows per expert
+    int32_t *s_eoff = lds + g.E;    // [E + 1] first row per expert
+    for (int e = tid; e < g.E; e += kFusedThreads)
+        s_tot[e] = tot[e];
+    if (tid < g.k) {
+        const int e = idx[t * g.k + tid];
+        s_e[tid] = e;
+        s_pre[tid] = ws[(int64_t)e * g.Gs + c];
+        s_cnt[tid] = 0;
+    }
+    __syncthreads();
+    block_exclusive_scan<kFusedThreads>(g, s_tot, s_eoff, s_wsum);
+    int ej[kFusedMaxK];
+#pragma unroll
+    for (int j = 0; j < kFusedMaxK; ++j)
+        ej[j] = j < g.k ? s_e[j] : -1;
+    // pairs of the chunk before (t, j) with expert e_j, by ballots
+    const int64_t p_beg = (int64_t)c * g.ct * g.k, p_t = t * g.k;
+    for (int64_t base = p_beg; base < p_t + g.k - 1; base += kFusedThreads) {
+        const int64_t p = base + tid;
+        const int id = p < p_t + g.k - 1 ? idx[p] : -1;
+#pragma unroll
+        for (int j = 0; j < kFusedMaxK; ++j) {
+            if (j < g.k) {   // uniform: every lane takes part in the ballot
+                const uint64_t bal = __ballot(p < p_t + j && id == ej[j]);
+                if (lane == 0 && bal != 0ull)
+                    atomicAdd(&s_cnt[j], (int)__popcll(bal));
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < g.k)
+        s_rows[tid] = s_eoff[s_e[tid]] + s_pre[tid] + s_cnt[tid];
+    __syncthreads();
+
+    // copy the slice to each row: a wave streams whole rows, 16 KiB per burst
+    const int c_beg = blockIdx.y * slice;
+    const int c_end = min(nvec, c_beg + slice);
+    const u32x4 *xr = x + t * nvec;
+    for (int d = wave; d < g.k; d += kFusedWaves) {
+        u32x4 *dst = recv + (int64_t)s_rows[d] * nvec;
+        for (int c0 = c_beg + lane; c0 < c_end; c0 += kWave * kFusedBurst) {
+            u32x4 v[kFusedBurst];
+#pragma unroll
+            for (int i = 0; i < kFusedBurst; ++i) {
+                const int cc = c0 + i * kWave;
+                if (cc < c_end)
+                    v[i] = xr[cc];
+            }
+#pragma unroll
+            for (int i = 0; i < kFusedBurst; ++i) {
+                const int cc = c0 + i * kWave;
+                if (cc < c_end)
+                    __builtin_nontemporal_store(v[i], dst + cc);
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------- single workgroup
@@ -620,6 +727,42 @@ size_t small_layout_lds(const Geometry &g)
     return bytes <= 64 * 1024 ? bytes : 0;
 }
 
+// LDS of an assign workgroup of nt threads, and the counting waves it uses:
+// nt / 64, halved until the LDS fits in 64 KB.
+size_t assign_lds(const Geometry &g, int nt, int &nww)
+{
+    const int ncol = g.E + g.R + g.H + 1;
+    const int kc = g.ct * g.k;
+    nww = nt / kWave;
+    for (;;) {
+        const size_t bytes =
+            (size_t)(2 * g.ct + 2 * ncol + g.E + 1 + g.H + 1 + 3 * kc + nww * (g.E + 1)) *
+            sizeof(int32_t);
+        if (bytes <= 64 * 1024 || nww == 1)
+            return bytes;
+        nww /= 2;
+    }
+}
+
+hipError_t launch_count(const Geometry &g, const int32_t *idx, const epx_layout &L,
+                        hipStream_t stream)
+{
+    const int ncol = g.E + g.R + g.H + 1;
+    const size_t lds = (size_t)(ncol + 3 * g.ct * g.k) * sizeof(int32_t);
+    hipLaunchKernelGGL(layout_count_kernel, dim3(g.G), dim3(kCountThreads), lds, stream, idx, g,
+                       L.workspace);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const Geometry &g, const epx_layout &L, hipStream_t stream)
+{
+    const int ncol = g.E + g.R + g.H + 1;
+    const int cols_per_block = 256 / kWave;
+    hipLaunchKernelGGL(layout_scan_kernel, dim3((ncol + cols_per_block - 1) / cols_per_block),
+                       dim3(256), 0, stream, g, L.workspace);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_layout(const Geometry &g, const int32_t *idx, const epx_layout &L,
@@ -631,38 +774,45 @@ hipError_t launch_layout(const Geometry &g, const int32_t *idx, const epx_layout
                            g, L);
         return hipGetLastError();
     }
-    const int ncol = g.E + g.R + g.H + 1;
-    const int kc = g.ct * g.k;
-    const size_t lds_count = (size_t)(ncol + 3 * kc) * sizeof(int32_t);
-    hipLaunchKernelGGL(layout_count_kernel, dim3(g.G), dim3(kCountThreads), lds_count, stream, idx,
-                       g, L.workspace);
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_count(g, idx, L, stream);
     if (err != hipSuccess)
         return err;
-    // counting waves: 8, halved until the assign workgroup's LDS fits in 64 KB
-    int nww = kAssignWaves;
-    size_t lds_assign = 0;
-    for (;;) {
-        lds_assign = (size_t)(2 * g.ct + 2 * ncol + g.E + 1 + g.H + 1 + 3 * kc + nww * (g.E + 1)) *
-                     sizeof(int32_t);
-        if (lds_assign <= 64 * 1024 || nww == 1)
-            break;
-        nww /= 2;
-    }
+    int nww = 0;
+    const size_t lds_assign = assign_lds(g, kAssignThreads, nww);
     if (g.G <= kSumsMaxG) {
         hipLaunchKernelGGL(layout_assign_kernel<true>, dim3(g.G), dim3(kAssignThreads), lds_assign,
                            stream, idx, g, (const int32_t *)L.workspace, L, nww);
         return hipGetLastError();
     }
-    const int cols_per_block = 256 / kWave;
-    hipLaunchKernelGGL(layout_scan_kernel, dim3((ncol + cols_per_block - 1) / cols_per_block),
-                       dim3(256), 0, stream, g, L.workspace);
-    err = hipGetLastError();
-    if (err != hipSuccess)
+    if ((err = launch_scan(g, L, stream)) != hipSuccess)
         return err;
     hipLaunchKernelGGL(layout_assign_kernel<false>, dim3(g.G), dim3(kAssignThreads), lds_assign,
                        stream, idx, g, (const int32_t *)L.workspace, L, nww);
     return hipGetLastError();
+}
+
+bool launch_layout_assign_dispatch(const Geometry &g, const int32_t *idx, const epx_layout &L,
+                                   const void *x, int32_t hidden, void *recv, hipStream_t stream,
+                                   hipError_t *err)
+{
+    if (g.relay || g.m != 1 || g.k > kFusedMaxK || g.T == 0 || small_layout_lds(g) > 0)
+        return false;
+    int nww = 0;
+    const size_t lds_assign = assign_lds(g, kFusedThreads, nww);
+    const size_t lds_tok = (2 * (size_t)g.E + 1) * sizeof(int32_t);
+    const size_t lds = lds_assign > lds_tok ? lds_assign : lds_tok;
+    if ((*err = launch_count(g, idx, L, stream)) != hipSuccess)
+        return true;
+    if ((*err = launch_scan(g, L, stream)) != hipSuccess)
+        return true;
+    const int nvec = hidden / 8;
+    const int slice = slice_width(g.T, nvec, kWave, 1 << 30, 2048);
+    const dim3 grid = item_grid((int64_t)g.G + g.T, (nvec + slice - 1) / slice);
+    hipLaunchKernelGGL(assign_copy_bf16_kernel, grid, dim3(kFusedThreads), lds, stream, idx, g,
+                       (const int32_t *)L.workspace, L, nww, (const u32x4 *)x, nvec, slice,
+                       (u32x4 *)recv);
+    *err = hipGetLastError();
+    return true;
 }
 
 }  // namespace epx
