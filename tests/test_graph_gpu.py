@@ -31,6 +31,7 @@ CASES = [
     ("decode_uniform", False, 4, True, False, False),
     ("decode_skewed", True, 1, True, True, False),
     ("rank_heavy", False, 1, False, True, False),
+    ("large_batch", False, 1, False, True, False),   # count, scan, assign-and-copy
     ("decode_skewed", True, 1, True, False, True),
     ("rank_light", True, 1, False, True, True),
 ]
