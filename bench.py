@@ -92,7 +92,7 @@ KERNEL_SOURCE = {"dispatch_bf16_kernel": "epx_dispatch.hip", "dispatch_fp8_kerne
                  "combine_kernel": "epx_combine.hip", "relay_fanout_kernel": "epx_relay.hip",
                  "relay_partials_kernel": "epx_relay.hip", "relay_finish_kernel": "epx_relay.hip",
                  "combine_group_kernel": "epx_combine.hip", "plan_swaps_kernel": "epx_balance.hip",
-                 "layout_dispatch_kernel": "epx_fused.hip", "assign_copy_bf16_kernel": "epx_layout.hip"}
+                 "layout_dispatch_kernel": "epx_fused.hip", "assign_copy_kernel": "epx_layout.hip"}
 
 
 def relay_receive_bytes(T, k, H, hidden, rows, fp8, f32_partials):
@@ -128,11 +128,12 @@ def kernel_sources_hash(kernel: str = "") -> str:
 def fused_kernel(T, k, E, relay, fp8):
     """The kernel that copies the rows in an epx_layout_dispatch call: the
     single-launch kernel at decode sizes, the assign-and-copy launch for
-    larger per-expert bf16 batches, else the plain dispatch kernel."""
+    larger batches with k <= 16 (bf16, or fp8 in relay mode), else the plain
+    dispatch kernel."""
     if T <= 1024 and T * k <= 4096 and k <= 16 and E <= 512:
         return "layout_dispatch_kernel"
-    if not relay and not fp8 and k <= 16:
-        return "assign_copy_bf16_kernel"
+    if k <= 16 and (relay or not fp8):
+        return "assign_copy_kernel"
     return "dispatch_fp8_kernel" if fp8 else "dispatch_bf16_kernel"
 
 
@@ -153,7 +154,7 @@ KERNEL_NAMES = ("dispatch_bf16_kernel", "dispatch_fp8_kernel", "combine_kernel",
                 "relay_fanout_kernel", "relay_partials_kernel", "relay_finish_kernel",
                 "layout_small_kernel", "layout_count_kernel", "layout_scan_kernel",
                 "layout_assign_kernel", "combine_group_kernel", "plan_swaps_kernel",
-                "layout_dispatch_kernel", "assign_copy_bf16_kernel")
+                "layout_dispatch_kernel", "assign_copy_kernel")
 
 
 def ingest_counters(fetch_csv: str, write_csv: str, tag: str, command: str) -> list:

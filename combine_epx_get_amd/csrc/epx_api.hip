@@ -257,7 +257,8 @@ epx_status epx_layout_dispatch(const epx_problem *p, const int32_t *topk_idx,
     if (g.T > 0 &&
         epx::launch_layout_dispatch(g, topk_idx, *layout, x, hidden, fp8, recv, recv_scales, s, &err))
         return from_hip(err);
-    if (!fp8 && epx::launch_layout_assign_dispatch(g, topk_idx, *layout, x, hidden, recv, s, &err))
+    if (epx::launch_layout_assign_dispatch(g, topk_idx, *layout, x, hidden, fp8, recv, recv_scales,
+                                           s, &err))
         return from_hip(err);
     if ((st = from_hip(epx::launch_layout(g, topk_idx, *layout, s))) != EPX_OK || g.T == 0)
         return st;

@@ -200,6 +200,51 @@ __device__ __forceinline__ uint32_t quantize4(float a, float b, float c, float d
     return e4m3_pair(qa, qb) | (e4m3_pair(qc, qd) << 16);
 }
 
+// Quantise chunks [c_beg, c_beg + n) of the bf16 row xr (8 channels per
+// 16-byte chunk) into LDS: 8 code bytes per chunk at s_codes (as u32x2) and
+// one scale per 128-channel block at s_scale. A 16-lane group owns one block
+// (its maximum by lane shuffles); each of the NT threads issues the loads of
+// up to PRE chunks before converting any. n and NT are multiples of 16, so
+// a 16-lane group is either all in range or all out. The caller
+// synchronises the workgroup before reading the codes.
+template <int NT, int PRE>
+__device__ __forceinline__ void quantize_slice_to_lds(const u32x4 *__restrict__ xr, int c_beg,
+                                                      int n, u32x2 *s_codes, float *s_scale)
+{
+    for (int base = 0; base < n; base += NT * PRE) {
+        u32x4 xv[PRE];
+#pragma unroll
+        for (int p = 0; p < PRE; ++p) {
+            const int i = base + p * NT + (int)threadIdx.x;
+            if (i < n)
+                xv[p] = xr[c_beg + i];
+        }
+#pragma unroll
+        for (int p = 0; p < PRE; ++p) {
+            const int i = base + p * NT + (int)threadIdx.x;
+            if (i >= n)
+                break;   // uniform over each 16-lane group, and later p are out too
+            const u32x4 v = xv[p];
+            const float f0 = bf16_lo(v.x), f1 = bf16_hi(v.x), f2 = bf16_lo(v.y), f3 = bf16_hi(v.y);
+            const float f4 = bf16_lo(v.z), f5 = bf16_hi(v.z), f6 = bf16_lo(v.w), f7 = bf16_hi(v.w);
+            float m = fmaxf(fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))),
+                            fmaxf(fmaxf(fabsf(f4), fabsf(f5)), fmaxf(fabsf(f6), fabsf(f7))));
+#pragma unroll
+            for (int dd = 8; dd > 0; dd >>= 1)
+                m = fmaxf(m, __shfl_xor(m, dd, 16));
+            const float s = m / 448.0f;
+            const bool zero = (m == 0.0f);
+            const float y = refined_reciprocal(s);
+            u32x2 q;
+            q.x = quantize4(f0, f1, f2, f3, s, y, zero);
+            q.y = quantize4(f4, f5, f6, f7, s, y, zero);
+            s_codes[i] = q;
+            if ((i & 15) == 0)
+                s_scale[i >> 4] = s;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- launch shapes
 // Column slices per token, each a whole number of `align` chunks: at least
 // `target` workgroups in all (small batches need slices to cover the GPU).

@@ -84,13 +84,13 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const epx_layout &L, const voi
 bool launch_layout_dispatch(const Geometry &g, const int32_t *idx, const epx_layout &L,
                             const void *x, int32_t hidden, bool fp8, void *recv, float *scales,
                             hipStream_t stream, hipError_t *err);
-// Per-expert bf16 layout and dispatch above the single-launch sizes: count,
-// scan, then one launch that assigns the rows and copies the tokens. False
-// (nothing launched) when it does not apply; *err receives the status
-// otherwise.
+// Layout and dispatch above the single-launch sizes (k <= 16, one expert
+// group; bf16, or fp8 in relay mode): count, scan, then one launch that
+// assigns the rows and copies the tokens. False (nothing launched) when it does not apply; *err receives the
+// status otherwise.
 bool launch_layout_assign_dispatch(const Geometry &g, const int32_t *idx, const epx_layout &L,
-                                   const void *x, int32_t hidden, void *recv, hipStream_t stream,
-                                   hipError_t *err);
+                                   const void *x, int32_t hidden, bool fp8, void *recv,
+                                   float *scales, hipStream_t stream, hipError_t *err);
 hipError_t launch_combine(const Geometry &g, const epx_layout &L, const void *y,
                           const float *w, int32_t hidden, void *out, hipStream_t stream);
 hipError_t launch_combine_group(const Geometry &g, const epx_layout &L, int group,

@@ -409,29 +409,42 @@ __global__ __launch_bounds__(kAssignThreads) void layout_assign_kernel(
 }
 
 // ---------------------------------------------------------------- assign + dispatch
-// Per-expert bf16 batches past the single-launch decode path: after the
-// count and scan launches, one launch both assigns the rows (items [0, G):
-// the chunk workgroups of the assign kernel, unchanged) and copies the
-// tokens (item G + t), so that no copy waits for an assign launch to end.
-// A token workgroup reads nothing the assign workgroups write: the row of
-// its pair (t, j) with expert e is the rows of the experts before e (an
-// exclusive scan of the column totals), plus the rows of e in earlier chunks
-// (the scan's prefix for t's chunk), plus the pairs of t's chunk before
-// (t, j) with expert e -- the assign kernel's row, bit for bit.
+// Batches past the single-launch decode path (k <= 16, one expert group;
+// bf16, or fp8 in relay mode):
+// after the count and scan launches, one launch both assigns the rows
+// (items [0, G): the chunk workgroups of the assign kernel, unchanged) and
+// copies the tokens (item G + t, one per column slice), so that no copy
+// waits for an assign launch to end. A token workgroup reads nothing the
+// assign workgroups write; its rows equal theirs bit for bit:
+//  * per-expert: the row of pair (t, j) with expert e is the rows of the
+//    experts before e (an exclusive scan of the column totals), plus the
+//    rows of e in earlier chunks (the scan's prefix for t's chunk), plus the
+//    pairs of t's chunk before (t, j) with expert e (ballots);
+//  * relay: the row of (t, host h) is the relay rows of the hosts before h,
+//    plus those of h in earlier chunks, plus the tokens of t's chunk before
+//    t that touch h (ballots over their host masks); -1 where t has no
+//    expert on h.
+// The copy is the dispatch kernel's: bf16 rows streamed 16 KiB per wave, or
+// the slice quantised once into LDS (E4M3 codes, per-block scales) and then
+// streamed to each row.
 constexpr int kFusedThreads = 256;
 constexpr int kFusedWaves = kFusedThreads / kWave;
-constexpr int kFusedBurst = 16;   // 16-byte chunks per lane per burst
+constexpr int kFusedBurst = 16;     // bf16: 16-byte chunks per lane per burst
+constexpr int kFusedBurstFp8 = 4;   // fp8: code vectors per lane per burst (from LDS)
+constexpr int kFusedPre = 4;        // fp8: chunks loaded per thread before converting
 constexpr int kFusedMaxK = 16;
 
-__global__ __launch_bounds__(kFusedThreads) void assign_copy_bf16_kernel(
+template <bool FP8>
+__global__ __launch_bounds__(kFusedThreads) void assign_copy_kernel(
     const int32_t *__restrict__ idx, Geometry g, const int32_t *__restrict__ ws, epx_layout L,
-    int nww, const u32x4 *__restrict__ x, int nvec, int slice, u32x4 *__restrict__ recv)
+    int nww, const u32x4 *__restrict__ x, int nvec, int slice, void *__restrict__ recv,
+    float *__restrict__ scales)
 {
     extern __shared__ __align__(16) int32_t lds[];
     __shared__ int32_t s_e[kFusedMaxK];
     __shared__ int32_t s_pre[kFusedMaxK];
     __shared__ int32_t s_cnt[kFusedMaxK];
-    __shared__ int32_t s_rows[kFusedMaxK];
+    __shared__ int32_t s_rows[kMaxHosts];   // k <= 16 expert rows or H <= 64 relay rows
     __shared__ int32_t s_wsum[kFusedWaves];
     const int64_t item = item_index();
     if (item < g.G) {
@@ -448,62 +461,125 @@ __global__ __launch_bounds__(kFusedThreads) void assign_copy_bf16_kernel(
         return;   // out-of-range ids: the assign workgroups report them, nothing moves
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int c = (int)(t / g.ct);
-    int32_t *s_tot = lds;           // [E] rows per expert
-    int32_t *s_eoff = lds + g.E;    // [E + 1] first row per expert
-    for (int e = tid; e < g.E; e += kFusedThreads)
-        s_tot[e] = tot[e];
-    if (tid < g.k) {
-        const int e = idx[t * g.k + tid];
-        s_e[tid] = e;
-        s_pre[tid] = ws[(int64_t)e * g.Gs + c];
-        s_cnt[tid] = 0;
-    }
-    __syncthreads();
-    block_exclusive_scan<kFusedThreads>(g, s_tot, s_eoff, s_wsum);
-    int ej[kFusedMaxK];
+    const int D = g.relay ? g.H : g.k;
+    if (!g.relay) {
+        int32_t *s_tot = lds;           // [E] rows per expert
+        int32_t *s_eoff = lds + g.E;    // [E + 1] first row per expert
+        for (int e = tid; e < g.E; e += kFusedThreads)
+            s_tot[e] = tot[e];
+        if (tid < g.k) {
+            const int e = idx[t * g.k + tid];
+            s_e[tid] = e;
+            s_pre[tid] = ws[(int64_t)e * g.Gs + c];
+            s_cnt[tid] = 0;
+        }
+        __syncthreads();
+        block_exclusive_scan<kFusedThreads>(g, s_tot, s_eoff, s_wsum);
+        int ej[kFusedMaxK];
 #pragma unroll
-    for (int j = 0; j < kFusedMaxK; ++j)
-        ej[j] = j < g.k ? s_e[j] : -1;
-    // pairs of the chunk before (t, j) with expert e_j, by ballots
-    const int64_t p_beg = (int64_t)c * g.ct * g.k, p_t = t * g.k;
-    for (int64_t base = p_beg; base < p_t + g.k - 1; base += kFusedThreads) {
-        const int64_t p = base + tid;
-        const int id = p < p_t + g.k - 1 ? idx[p] : -1;
+        for (int j = 0; j < kFusedMaxK; ++j)
+            ej[j] = j < g.k ? s_e[j] : -1;
+        // pairs of the chunk before (t, j) with expert e_j
+        const int64_t p_beg = (int64_t)c * g.ct * g.k, p_t = t * g.k;
+        for (int64_t base = p_beg; base < p_t + g.k - 1; base += kFusedThreads) {
+            const int64_t p = base + tid;
+            const int id = p < p_t + g.k - 1 ? idx[p] : -1;
 #pragma unroll
-        for (int j = 0; j < kFusedMaxK; ++j) {
-            if (j < g.k) {   // uniform: every lane takes part in the ballot
-                const uint64_t bal = __ballot(p < p_t + j && id == ej[j]);
-                if (lane == 0 && bal != 0ull)
-                    atomicAdd(&s_cnt[j], (int)__popcll(bal));
+            for (int j = 0; j < kFusedMaxK; ++j) {
+                if (j < g.k) {   // uniform: every lane takes part in the ballot
+                    const uint64_t bal = __ballot(p < p_t + j && id == ej[j]);
+                    if (lane == 0 && bal != 0ull)
+                        atomicAdd(&s_cnt[j], (int)__popcll(bal));
+                }
             }
         }
+        __syncthreads();
+        if (tid < g.k)
+            s_rows[tid] = s_eoff[s_e[tid]] + s_pre[tid] + s_cnt[tid];
+    } else if (wave == 0) {
+        // lane i < nb holds the host mask of the chunk's token t0 + i, lane
+        // nb that of t itself (a chunk holds at most 32 tokens for k <= 16)
+        const int64_t t0 = (int64_t)c * g.ct;
+        const int nb = (int)(t - t0);
+        uint64_t mask = 0;
+        if (lane <= nb)
+            for (int j = 0; j < g.k; ++j) {
+                const int e = idx[(t0 + lane) * g.k + j];
+                mask |= 1ull << g.div_rph.div(g.div_epr.div(e));
+            }
+        const uint32_t mlo = __shfl((uint32_t)mask, nb), mhi = __shfl((uint32_t)(mask >> 32), nb);
+        const uint64_t mine = ((uint64_t)mhi << 32) | mlo;
+        const int hv = lane < g.H ? tot[g.E + g.R + lane] : 0;
+        const int hoff = wave_inclusive_scan(hv) - hv;   // relay rows of the hosts before lane's
+        const int pre = lane < g.H ? ws[(int64_t)(g.E + g.R + lane) * g.Gs + c] : 0;
+        int before = 0;
+        for (int h = 0; h < g.H; ++h) {
+            const uint64_t bal = __ballot(lane < nb && ((mask >> h) & 1ull));
+            if (lane == h)
+                before = (int)__popcll(bal);
+        }
+        if (lane < g.H)
+            s_rows[lane] = ((mine >> lane) & 1ull) ? hoff + pre + before : -1;
     }
     __syncthreads();
-    if (tid < g.k)
-        s_rows[tid] = s_eoff[s_e[tid]] + s_pre[tid] + s_cnt[tid];
-    __syncthreads();
 
-    // copy the slice to each row: a wave streams whole rows, 16 KiB per burst
     const int c_beg = blockIdx.y * slice;
     const int c_end = min(nvec, c_beg + slice);
     const u32x4 *xr = x + t * nvec;
-    for (int d = wave; d < g.k; d += kFusedWaves) {
-        u32x4 *dst = recv + (int64_t)s_rows[d] * nvec;
-        for (int c0 = c_beg + lane; c0 < c_end; c0 += kWave * kFusedBurst) {
-            u32x4 v[kFusedBurst];
+    if (!FP8) {
+        // a wave streams whole rows, 16 KiB per burst
+        for (int d = wave; d < D; d += kFusedWaves) {
+            const int r = s_rows[d];
+            if (r < 0)
+                continue;
+            u32x4 *dst = (u32x4 *)recv + (int64_t)r * nvec;
+            for (int c0 = c_beg + lane; c0 < c_end; c0 += kWave * kFusedBurst) {
+                u32x4 v[kFusedBurst];
 #pragma unroll
-            for (int i = 0; i < kFusedBurst; ++i) {
+                for (int i = 0; i < kFusedBurst; ++i) {
+                    const int cc = c0 + i * kWave;
+                    if (cc < c_end)
+                        v[i] = xr[cc];
+                }
+#pragma unroll
+                for (int i = 0; i < kFusedBurst; ++i) {
+                    const int cc = c0 + i * kWave;
+                    if (cc < c_end)
+                        __builtin_nontemporal_store(v[i], dst + cc);
+                }
+            }
+        }
+        return;
+    }
+    // fp8: the slice's codes and scales in LDS past the scan's arrays
+    const int n = c_end - c_beg;
+    u32x4 *s_codes = (u32x4 *)(lds + ((2 * g.E + 1 + 3) & ~3));
+    float *s_scale = (float *)(s_codes + (slice >> 1));
+    quantize_slice_to_lds<kFusedThreads, kFusedPre>(xr, c_beg, n, (u32x2 *)s_codes, s_scale);
+    __syncthreads();
+    const int nq = n >> 1, nblk = n >> 4, row_vec = nvec >> 1, row_blk = nvec >> 4;
+    for (int d = wave; d < D; d += kFusedWaves) {
+        const int r = s_rows[d];
+        if (r < 0)
+            continue;
+        u32x4 *dst = (u32x4 *)recv + (int64_t)r * row_vec + (c_beg >> 1);
+        for (int c0 = lane; c0 < nq; c0 += kWave * kFusedBurstFp8) {
+            u32x4 v[kFusedBurstFp8];
+#pragma unroll
+            for (int i = 0; i < kFusedBurstFp8; ++i) {
                 const int cc = c0 + i * kWave;
-                if (cc < c_end)
-                    v[i] = xr[cc];
+                if (cc < nq)
+                    v[i] = s_codes[cc];
             }
 #pragma unroll
-            for (int i = 0; i < kFusedBurst; ++i) {
+            for (int i = 0; i < kFusedBurstFp8; ++i) {
                 const int cc = c0 + i * kWave;
-                if (cc < c_end)
+                if (cc < nq)
                     __builtin_nontemporal_store(v[i], dst + cc);
             }
         }
+        for (int bk = lane; bk < nblk; bk += kWave)
+            scales[(int64_t)r * row_blk + (c_beg >> 4) + bk] = s_scale[bk];
     }
 }
 
@@ -792,25 +868,42 @@ hipError_t launch_layout(const Geometry &g, const int32_t *idx, const epx_layout
 }
 
 bool launch_layout_assign_dispatch(const Geometry &g, const int32_t *idx, const epx_layout &L,
-                                   const void *x, int32_t hidden, void *recv, hipStream_t stream,
-                                   hipError_t *err)
+                                   const void *x, int32_t hidden, bool fp8, void *recv,
+                                   float *scales, hipStream_t stream, hipError_t *err)
 {
-    if (g.relay || g.m != 1 || g.k > kFusedMaxK || g.T == 0 || small_layout_lds(g) > 0)
+    // Per-expert fp8 keeps the separate launches: a token's quantisation
+    // followed by 8 row stores in one workgroup measured slower (4096 x 7168:
+    // 156.7 against 153.4 us per layer under graph replay) than the dispatch
+    // kernel's column slices, which overlap the two; relay fp8 (about 3.6
+    // rows per token) gains (131.8 against 132.9 us).
+    if (g.m != 1 || g.k > kFusedMaxK || g.T == 0 || small_layout_lds(g) > 0 || (fp8 && !g.relay))
         return false;
     int nww = 0;
     const size_t lds_assign = assign_lds(g, kFusedThreads, nww);
-    const size_t lds_tok = (2 * (size_t)g.E + 1) * sizeof(int32_t);
+    const int nvec = hidden / 8;
+    // column slices only for small batches (about 2048 workgroups): every
+    // slice workgroup repeats the derivation of its token's rows
+    const int slice = fp8 ? slice_width(g.T, nvec, 16, 4096, 2048)
+                          : slice_width(g.T, nvec, kWave, 1 << 30, 2048);
+    size_t lds_tok = (size_t)((2 * g.E + 1 + 3) & ~3) * sizeof(int32_t);
+    if (fp8)
+        lds_tok += (size_t)slice * 8 + (size_t)(slice / 16) * sizeof(float);
     const size_t lds = lds_assign > lds_tok ? lds_assign : lds_tok;
+    if (lds > 64 * 1024)
+        return false;
     if ((*err = launch_count(g, idx, L, stream)) != hipSuccess)
         return true;
     if ((*err = launch_scan(g, L, stream)) != hipSuccess)
         return true;
-    const int nvec = hidden / 8;
-    const int slice = slice_width(g.T, nvec, kWave, 1 << 30, 2048);
     const dim3 grid = item_grid((int64_t)g.G + g.T, (nvec + slice - 1) / slice);
-    hipLaunchKernelGGL(assign_copy_bf16_kernel, grid, dim3(kFusedThreads), lds, stream, idx, g,
-                       (const int32_t *)L.workspace, L, nww, (const u32x4 *)x, nvec, slice,
-                       (u32x4 *)recv);
+    if (fp8)
+        hipLaunchKernelGGL(assign_copy_kernel<true>, grid, dim3(kFusedThreads), lds, stream, idx, g,
+                           (const int32_t *)L.workspace, L, nww, (const u32x4 *)x, nvec, slice,
+                           recv, scales);
+    else
+        hipLaunchKernelGGL(assign_copy_kernel<false>, grid, dim3(kFusedThreads), lds, stream, idx,
+                           g, (const int32_t *)L.workspace, L, nww, (const u32x4 *)x, nvec, slice,
+                           recv, scales);
     *err = hipGetLastError();
     return true;
 }

@@ -12,7 +12,7 @@
  *   epx_dispatch     -- token rows -> per-expert rows (Mode 1) or one row per
  *                       destination host (Mode 2 relay), bf16 or fp8
  *   epx_layout_dispatch -- the two above in one call (one launch for decode
- *                       batches, fewer launches for larger per-expert ones)
+ *                       batches, fewer launches for larger ones)
  *   epx_combine      -- k expert outputs per token -> weighted sum, bf16
  *   epx_relay_fanout, epx_combine_relay_partials, epx_combine_relay_finish
  *                    -- the relay's receive side and its two-level combine
@@ -208,11 +208,12 @@ EPX_API epx_status epx_combine(const epx_problem *p, const epx_layout *layout, c
  * enough that every dispatch workgroup recomputes the part of it that its
  * token needs, so the two steps run as one launch with no dependency between
  * workgroups: used when T <= 1024, T*k <= 4096, k <= 16 and E <= 512 (and
- * the kernel's LDS fits in 60 KB). Larger per-expert bf16 batches with
- * k <= 16 (one expert group) take the layout's count and scan launches and
- * then one launch in which the row assignment and the token copies run side
- * by side (each token workgroup derives its own rows from the scan); every
- * other case makes the layout and dispatch launches. Arguments, alignment
+ * the kernel's LDS fits in 60 KB). Larger batches with k <= 16 and one
+ * expert group (bf16 in either mode, fp8 in HOST_RELAY mode) take the
+ * layout's count and scan launches and then one launch in which the row
+ * assignment and the token copies run side by side (each token workgroup
+ * derives its own rows from the scan); every other case makes the layout
+ * and dispatch launches. Arguments, alignment
  * and capacity rules are those of the two calls; the layout's workspace may
  * go unused. Errors: those of either call, checked before anything is
  * launched. */

@@ -32,6 +32,7 @@ CASES = [
     ("decode_skewed", True, 1, True, True, False),
     ("rank_heavy", False, 1, False, True, False),
     ("large_batch", False, 1, False, True, False),   # count, scan, assign-and-copy
+    ("fp8_dispatch", True, 1, True, True, False),    # the same in relay mode, fp8
     ("decode_skewed", True, 1, True, False, True),
     ("rank_light", True, 1, False, True, True),
 ]

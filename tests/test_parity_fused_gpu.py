@@ -106,7 +106,9 @@ def run_fused(epx, x_bits, idx, E, R, H, s, relay, dtype, m=1, what=""):
 DECODE = [("decode_uniform", "per_expert"), ("decode_skewed", "per_expert"),
           ("decode_skewed", "relay"), ("decode_skewed_s06", "relay"), ("tiny", "per_expert"),
           ("tiny", "relay"), ("rank_light", "per_expert"), ("rank_light", "relay"),
-          ("rank_heavy", "per_expert"), ("rank_balanced", "relay")]
+          ("rank_heavy", "per_expert"), ("rank_balanced", "relay"),
+          # past the decode limits: count, scan and the assign-and-copy launch
+          ("large_batch", "per_expert"), ("large_batch", "relay"), ("fp8_dispatch", "relay")]
 
 
 @pytest.mark.parametrize("name,mode", DECODE)
@@ -133,8 +135,8 @@ SHAPES = [
     (513, 8, 256, 32, 4, 2, 256, "uniform"),     # T*k > 4096: two launches
     (100, 4, 1024, 32, 4, 2, 128, "uniform"),    # E > 512: two launches
     (1025, 2, 16, 4, 2, 1, 128, "uniform"),      # T > 1024: two launches
-    # past the decode limits, per-expert bf16 takes count, scan and one
-    # assign-and-copy launch (relay and fp8 the layout and dispatch launches)
+    # past the decode limits (k <= 16) the call takes count, scan and one
+    # assign-and-copy launch
     (4096, 8, 256, 16, 2, 3, 7168, "uniform"),   # the 4096-token batch
     (700, 8, 256, 32, 4, 1, 1024, "zipf"),       # column slices (T < 2048)
     (2000, 16, 2048, 64, 8, 5, 256, "zipf"),     # k = 16, E = 2048
@@ -179,30 +181,38 @@ def test_fused_duplicate_ids(epx, relay):
     run_fused(epx, x, np.full((T, k), 11, np.int32), E, R, H, 1, relay, "bf16", what="one expert")
 
 
-def test_fused_duplicate_ids_large(epx):
+@pytest.mark.parametrize("relay", [False, True])
+def test_fused_duplicate_ids_large(epx, relay):
     """Past the decode limits: many pairs of a token on one expert."""
     rng = np.random.Generator(np.random.PCG64(19))
     T, k, E, R, H, hidden = 2000, 8, 16, 4, 2, 256
     x = W.f32_to_bf16_bits(rng.standard_normal((T, hidden), dtype=np.float32))
     idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
-    run_fused(epx, x, idx, E, R, H, 3, False, "bf16", what="duplicates large")
-    run_fused(epx, x, np.full((T, k), 5, np.int32), E, R, H, 0, False, "bf16", what="one expert large")
+    run_fused(epx, x, idx, E, R, H, 3, relay, "bf16", what="duplicates large")
+    run_fused(epx, x, idx, E, R, H, 3, relay, "fp8", what="duplicates large/fp8")
+    run_fused(epx, x, np.full((T, k), 5, np.int32), E, R, H, 0, relay, "bf16", what="one expert large")
 
 
-def test_fused_out_of_range_ids_large(epx):
+@pytest.mark.parametrize("relay", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_fused_out_of_range_ids_large(epx, relay, dtype):
     """Past the decode limits: bad ids are counted and nothing is copied."""
     T, k, E, R, H, hidden = 1000, 8, 64, 8, 2, 128
     rng = np.random.Generator(np.random.PCG64(23))
     idx = W.draw_routing(rng, T, E, k, "uniform", 1.0)
     idx[5, 3] = E
     idx[999, 7] = -2
-    p = epx.make_problem(T, k, E, R, H, 0, epx.MODE_PER_EXPERT)
+    p = epx.make_problem(T, k, E, R, H, 0, epx.MODE_HOST_RELAY if relay else epx.MODE_PER_EXPERT)
+    cap = epx.relay_capacity(p) if relay else T * k
     L = _fresh_layout(epx, p)
-    recv, _ = _recv(T * k, hidden, "bf16")
+    recv, sc = _recv(cap, hidden, dtype)
     epx.epx_layout_dispatch(p, _dev(idx), L, torch.ones((T, hidden), dtype=torch.bfloat16, device="cuda"),
-                            epx.BF16, recv)
+                            epx.BF16 if dtype == "bf16" else epx.FP8_E4M3, recv, sc)
     assert epx.epx_read_error(L) == 2
-    assert np.all(_bits(recv) == np.uint16(SENTINEL_BF16 & 0xFFFF))
+    if dtype == "bf16":
+        assert np.all(_bits(recv) == np.uint16(SENTINEL_BF16 & 0xFFFF))
+    else:
+        assert np.all(recv.cpu().numpy() == SENTINEL_U8) and np.all(sc.cpu().numpy() == -1.0)
 
 
 @pytest.mark.parametrize("relay", [False, True])
