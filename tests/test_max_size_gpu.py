@@ -70,7 +70,20 @@ def test_max_tokens(epx, relay):
     x = W.f32_to_bf16_bits(rng.standard_normal((T, h), dtype=np.float32))
     cap = epx.relay_capacity(p) if relay else T * k
     recv = torch.empty((cap, h), dtype=torch.bfloat16, device="cuda")
-    epx.epx_dispatch(p, L, _dev(x.view(np.int16)).view(torch.bfloat16), epx.BF16, recv)
+    x_dev = _dev(x.view(np.int16)).view(torch.bfloat16)
+    epx.epx_dispatch(p, L, x_dev, epx.BF16, recv)
+
+    # the fused call (count, scan, then assignment and copies in one launch)
+    # gives the same layout and rows
+    L2 = epx.Layout(p)
+    recv2 = torch.empty_like(recv)
+    epx.epx_layout_dispatch(p, _dev(idx), L2, x_dev, epx.BF16, recv2)
+    torch.cuda.synchronize()
+    used = int(L["totals"][1 if relay else 0])
+    for name in ("slot", "row_token", "expert_offset", "totals") + (("relay_slot", "relay_token") if relay else ()):
+        assert torch.equal(L2[name], L[name]), name
+    assert torch.equal(recv2[:used].view(torch.int16), recv[:used].view(torch.int16))
+    del L2, recv2
     y = W.f32_to_bf16_bits(rng.standard_normal((T * k, h), dtype=np.float32))
     w = rng.random((T, k), dtype=np.float32)
     out = torch.empty((T, h), dtype=torch.bfloat16, device="cuda")
