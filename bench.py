@@ -270,7 +270,7 @@ def main(argv=None) -> int:
                          "dispatches, M group combines (per-expert mode)")
     ap.add_argument("--fused", action="store_true",
                     help="layout and dispatch in one call (epx_layout_dispatch: one launch for "
-                         "decode-sized batches)")
+                         "decode-sized batches, assignment and copies in one launch above)")
     ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=None,
                     help="also time layers captured in a HIP graph (16 per graph) and replayed: the "
                          "layer time without per-launch host overhead (default: on, except with "

@@ -182,7 +182,8 @@ def epx_dispatch(problem: epx_problem, layout: Layout, x: torch.Tensor, out_dtyp
 def epx_layout_dispatch(problem: epx_problem, topk_idx: torch.Tensor, layout: Layout, x: torch.Tensor,
                         out_dtype: int, recv: torch.Tensor, recv_scales: Optional[torch.Tensor] = None,
                         stream=None) -> None:
-    """epx_get_layout then epx_dispatch, as one launch for decode-sized batches."""
+    """epx_get_layout then epx_dispatch in one call: one launch for decode-sized
+    batches, the row assignment and the copies in one launch for larger ones."""
     _need(topk_idx, torch.int32, "topk_idx", 2)
     if tuple(topk_idx.shape) != (problem.num_tokens, problem.topk):
         raise ValueError(f"topk_idx shape {tuple(topk_idx.shape)} != (T, k)")
