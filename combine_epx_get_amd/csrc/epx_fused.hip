@@ -379,38 +379,7 @@ __device__ void token_rows(int t, const int32_t *__restrict__ idx, const Geometr
     const int n = c_end - c_beg;
     u32x4 *s_codes = (u32x4 *)lds;
     float *s_scale = (float *)(s_codes + (slice >> 1));
-    for (int base = 0; base < n; base += kFThreads * kFPre) {
-        u32x4 xv[kFPre];
-#pragma unroll
-        for (int p = 0; p < kFPre; ++p) {
-            const int i = base + p * kFThreads + tid;
-            if (i < n)
-                xv[p] = xr[c_beg + i];
-        }
-#pragma unroll
-        for (int p = 0; p < kFPre; ++p) {
-            const int i = base + p * kFThreads + tid;
-            if (i >= n)
-                break;   // uniform over each 16-lane group (n and kFThreads are multiples of 16)
-            const u32x4 v = xv[p];
-            const float f0 = bf16_lo(v.x), f1 = bf16_hi(v.x), f2 = bf16_lo(v.y), f3 = bf16_hi(v.y);
-            const float f4 = bf16_lo(v.z), f5 = bf16_hi(v.z), f6 = bf16_lo(v.w), f7 = bf16_hi(v.w);
-            float m = fmaxf(fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))),
-                            fmaxf(fmaxf(fabsf(f4), fabsf(f5)), fmaxf(fabsf(f6), fabsf(f7))));
-#pragma unroll
-            for (int dd = 8; dd > 0; dd >>= 1)
-                m = fmaxf(m, __shfl_xor(m, dd, 16));
-            const float s = m / 448.0f;
-            const bool zero = (m == 0.0f);
-            const float y = refined_reciprocal(s);
-            u32x2 q;
-            q.x = quantize4(f0, f1, f2, f3, s, y, zero);
-            q.y = quantize4(f4, f5, f6, f7, s, y, zero);
-            ((u32x2 *)s_codes)[i] = q;
-            if ((i & 15) == 0)
-                s_scale[i >> 4] = s;
-        }
-    }
+    quantize_slice_to_lds<kFThreads, kFPre>(xr, c_beg, n, (u32x2 *)s_codes, s_scale);
     __syncthreads();
     const int nq = n >> 1, nblk = n >> 4, row_vec = nvec >> 1, row_blk = nvec >> 4;
     const int len = ((nq + wpr - 1) / wpr + kWave - 1) / kWave * kWave;
