@@ -92,7 +92,9 @@ KERNEL_SOURCE = {"dispatch_bf16_kernel": "epx_dispatch.hip", "dispatch_fp8_kerne
                  "combine_kernel": "epx_combine.hip", "relay_fanout_kernel": "epx_relay.hip",
                  "relay_partials_kernel": "epx_relay.hip", "relay_finish_kernel": "epx_relay.hip",
                  "combine_group_kernel": "epx_combine.hip", "plan_swaps_kernel": "epx_balance.hip",
-                 "layout_dispatch_kernel": "epx_fused.hip", "assign_copy_kernel": "epx_layout.hip"}
+                 "layout_dispatch_kernel": "epx_fused.hip", "assign_copy_kernel": "epx_layout.hip",
+                 "layout_small_kernel": "epx_layout.hip", "layout_count_kernel": "epx_layout.hip",
+                 "layout_scan_kernel": "epx_layout.hip", "layout_assign_kernel": "epx_layout.hip"}
 
 
 def relay_receive_bytes(T, k, H, hidden, rows, fp8, f32_partials):
