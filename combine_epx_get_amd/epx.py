@@ -131,8 +131,16 @@ class Layout:
         return self.tensors[name][: self.sizes[name]]
 
 
+# The current stream's raw handle: torch's own accessor costs about 0.1 us
+# per call against about 3 us for torch.cuda.current_stream() (measured on
+# MI355X), which is a third of a decode-sized call's host time.
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream) -> int:
     if stream is None:
+        if _raw_current_stream is not None:
+            return _raw_current_stream(torch.cuda.current_device())
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 

@@ -153,3 +153,13 @@ def test_graph_replays_match_eager(epx, case):
             if a.dtype == np.float32:
                 a, b = a.view(np.uint32), b.view(np.uint32)
             assert np.array_equal(a, b), (case, rep, n)
+
+
+def test_current_stream_handle(epx):
+    """The binding launches on torch's current stream: the raw handle it reads
+    is that stream's, on the default stream and inside a side-stream context."""
+    assert epx._stream(None) == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert epx._stream(None) == side.cuda_stream == torch.cuda.current_stream().cuda_stream
+    assert epx._stream(side) == side.cuda_stream
