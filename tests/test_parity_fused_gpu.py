@@ -170,6 +170,18 @@ def test_fused_expert_groups(epx, m):
     run_fused(epx, x, idx, E, R, H, 5, False, "fp8", m=m, what=f"groups {m}/fp8")
 
 
+def test_fused_expert_groups_large(epx):
+    """Past the decode limits, expert groups take the layout and dispatch
+    launches inside the call."""
+    rng = np.random.Generator(np.random.PCG64(44))
+    T, k, E, R, H, hidden = 1500, 8, 256, 16, 2, 256
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, hidden), dtype=np.float32))
+    idx = W.draw_routing(rng, T, E, k, "uniform", 1.0)
+    print("[fused] groups m=2, 1500 tokens", flush=True)
+    run_fused(epx, x, idx, E, R, H, 3, False, "bf16", m=2, what="groups 2 large")
+    run_fused(epx, x, idx, E, R, H, 3, False, "fp8", m=2, what="groups 2 large/fp8")
+
+
 @pytest.mark.parametrize("relay", [False, True])
 def test_fused_duplicate_ids(epx, relay):
     rng = np.random.Generator(np.random.PCG64(9))
