@@ -278,6 +278,35 @@ def test_repeat_runs_are_bitwise_identical(epx):
         assert np.array_equal(outs[0][n], outs[1][n]) and np.array_equal(outs[0][n], outs[2][n]), n
 
 
+@pytest.mark.parametrize("relay", [False, True])
+def test_repeat_layer_runs_are_bitwise_identical(epx, relay):
+    """Three runs of the whole layer through the fused call (4096 tokens: the
+    count, scan and assign-and-copy launches) and the combine give the same
+    bytes, layout arrays included."""
+    w = W.WORKLOADS["large_batch"]
+    d = W.make_inputs(w)
+    T, k, h = d["T"], w.topk, w.hidden
+    p = epx.make_problem(T, k, w.num_experts, w.num_ranks, w.num_hosts, 0,
+                         epx.MODE_HOST_RELAY if relay else epx.MODE_PER_EXPERT)
+    cap = epx.relay_capacity(p) if relay else T * k
+    idx, x = _dev(d["topk_idx"]), _bf16_dev(d["x"])
+    wts = _dev(d["topk_weights"])
+    y = _bf16_dev(W.random_bf16((T * k, h), seed=11))
+    runs = []
+    for _ in range(3):
+        L = epx.Layout(p)
+        recv = torch.zeros((cap, h), dtype=torch.bfloat16, device="cuda")
+        out = torch.zeros((T, h), dtype=torch.bfloat16, device="cuda")
+        epx.epx_layout_dispatch(p, idx, L, x, epx.BF16, recv)
+        epx.epx_combine(p, L, y, wts, out)
+        torch.cuda.synchronize()
+        runs.append((layout_np(epx, L, relay), _bits(recv), _bits(out)))
+    for lay, rows, o in runs[1:]:
+        for n in lay:
+            assert np.array_equal(lay[n], runs[0][0][n]), n
+        assert np.array_equal(rows, runs[0][1]) and np.array_equal(o, runs[0][2])
+
+
 def test_e4m3_conversion_exhaustive_vs_oracle(epx):
     """The kernel's float32 -> E4M3FN conversion on every non-negative finite
     float32 pattern, and a sample of negatives (the oracle's converter is
