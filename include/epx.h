@@ -180,7 +180,10 @@ EPX_API epx_status epx_get_layout(const epx_problem *p, const int32_t *topk_idx,
  *  hidden       multiple of 8 (bf16) or of 128 (fp8)
  *  capacity_rows >= T*k (PER_EXPERT) or >= T*min(k, H) (HOST_RELAY)
  * Rows are written at the layout's slots (PER_EXPERT) or relay slots
- * (HOST_RELAY); other rows of recv are left untouched. Errors: EPX_ERR_ARG
+ * (HOST_RELAY); other rows of recv are left untouched. The layout must come
+ * from epx_get_layout (or epx_layout_dispatch) with the same problem, ordered
+ * before this call; the host cannot check its contents, and a layout made
+ * for another problem can hold rows past capacity_rows. Errors: EPX_ERR_ARG
  * (dtype, hidden, pointers, 16-byte alignment), EPX_ERR_CAPACITY (recv too
  * small); after a layout that saw bad ids nothing is written. */
 EPX_API epx_status epx_dispatch(const epx_problem *p, const epx_layout *layout, const void *x,
@@ -193,7 +196,8 @@ EPX_API epx_status epx_dispatch(const epx_problem *p, const epx_layout *layout, 
  * expert outputs of each token gathered from the per-expert rows of y
  * (bf16 [y_rows, hidden], y_rows >= T*k) and summed in float32 as
  * acc = fma(w, y, acc) for j = 0..k-1 from +0, rounded to bf16 (nearest
- * even). Weights are used as given. hidden must be a multiple of 8.
+ * even). Weights are used as given. hidden must be a multiple of 8. The
+ * layout must come from the same problem (as for epx_dispatch).
  * Errors: EPX_ERR_ARG (hidden, pointers, alignment), EPX_ERR_CAPACITY
  * (y_rows < T*k); after a layout that saw bad ids nothing is written. */
 EPX_API epx_status epx_combine(const epx_problem *p, const epx_layout *layout, const void *y,
