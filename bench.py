@@ -470,19 +470,21 @@ def main(argv=None) -> int:
     if args.graph and planner:
         print("--graph does not capture the swap planner's alternating placement", file=sys.stderr)
         return 2
-    if args.graph if args.graph is not None else not planner:
+
+    def time_graph(layer):
+        """µs per layer from replays of GRAPH_STEPS layers captured in one
+        HIP graph, so that one replay's host cost is spread over many layers
+        and the time is the GPU's."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step()
+            layer()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        # GRAPH_STEPS layers per graph, so that one replay's host cost is
-        # spread over many layers and the time is the GPU's
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for _ in range(GRAPH_STEPS):
-                step()
+                layer()
         replays = max(1, args.steps // GRAPH_STEPS)
         for _ in range(max(1, args.warmup // GRAPH_STEPS)):
             graph.replay()
@@ -493,7 +495,19 @@ def main(argv=None) -> int:
             graph.replay()
         g1.record()
         torch.cuda.synchronize()
-        graph_us = g0.elapsed_time(g1) * 1e3 / (replays * GRAPH_STEPS)
+        del graph
+        return g0.elapsed_time(g1) * 1e3 / (replays * GRAPH_STEPS)
+
+    graph_fused_us = None
+    if args.graph if args.graph is not None else not planner:
+        graph_us = time_graph(step)
+        if not fused and m == 1 and not receive:
+            # the same layer with layout and dispatch as one epx_layout_dispatch call
+            def fused_layer():
+                stream = torch.cuda.current_stream()
+                epx.epx_layout_dispatch(p, idx, L, x, out_dtype, recv, scales, stream)
+                epx.epx_combine(p, L, y, wts, out, stream)
+            graph_fused_us = time_graph(fused_layer)
 
     lay_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     plan_ms = np.array([e[1].elapsed_time(e[6]) for e in evs])
@@ -597,6 +611,7 @@ def main(argv=None) -> int:
         "event_every": every,
         "us_per_layer": round(us_layer, 2),
         **({"us_per_layer_graph": round(graph_us, 2)} if graph_us is not None else {}),
+        **({"us_per_layer_graph_fused": round(graph_fused_us, 2)} if graph_fused_us is not None else {}),
         "pct_of_peak_layer": round(100 * layer_bytes / (us_layer * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
         "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for n, v in per_kernel.items()},
