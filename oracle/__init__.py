@@ -16,7 +16,11 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                     section 3.2; the worked example of the DeepEP issue.
   dispatch_bf16  -- row equality with the token's row (definition) on small inputs.
   dispatch_fp8   -- converter exhaustive vs torch's float8_e4m3fn cast; block
-                    properties (amax code is 448, error bound of a 3-bit mantissa).
+                    properties (amax code is 448, error bound of a 3-bit mantissa);
+                    scale and quotient by golden blocks whose codes are derived in
+                    exact rational arithmetic (s = RNE32(amax/448), RNE32(x/s)) and
+                    that x*(448/amax), x*(1/s) and amax*(1/448) all fail
+                    (tests/golden/fp8_quotient_blocks.json).
   combine        -- float64 sum within the float32 error bound; exact special cases.
   relay_fanout   -- equals the per-expert dispatch row for row (two independent
                     definitions); membership by host brute force.

@@ -56,6 +56,15 @@ MUTANTS = [
     ("fp8 scale constant",
      "            float s = a / 448.0f;",
      "            float s = a / 447.0f;"),
+    ("fp8 quotient as x times 448/amax",
+     "                    q[c] = oracle_f32_to_e4m3(v / s);",
+     "                    q[c] = oracle_f32_to_e4m3(v * (448.0f / a));"),
+    ("fp8 quotient as x times the reciprocal of the scale",
+     "                    q[c] = oracle_f32_to_e4m3(v / s);",
+     "                    q[c] = oracle_f32_to_e4m3(v * (1.0f / s));"),
+    ("fp8 scale as amax times 1/448",
+     "            float s = a / 448.0f;",
+     "            float s = a * (1.0f / 448.0f);"),
     ("fp8 amax without abs",
      "                if (fabsf(v) > a)\n                    a = fabsf(v);",
      "                if (v > a)\n                    a = v;"),
@@ -151,6 +160,7 @@ def _pins():
     calls.append(TN.test_bf16_rounding_vs_torch)
     calls.append(lambda: TN.test_fp8_block_properties(False))
     calls.append(lambda: TN.test_fp8_block_properties(True))
+    calls.append(TN.test_fp8_quotient_golden_blocks)
     calls.append(lambda: TN.test_dispatch_bf16_rows_are_token_rows(False))
     calls.append(lambda: TN.test_dispatch_bf16_rows_are_token_rows(True))
     calls.append(TN.test_combine_within_float32_bound_of_float64_sum)

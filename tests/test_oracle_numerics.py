@@ -253,3 +253,63 @@ def test_combine_config_rule_closed_form():
     exact = xf * fac[:, None]
     mag = np.abs(xf) * (np.abs(d["topk_weights"]) * (1 + d["topk_idx"] / 16.0)).sum(1)[:, None]
     assert np.all(np.abs(out - exact) <= 2.0 ** -7 * mag + 1e-30)
+
+
+# ---------------------------------------------------------------- fp8 quotient (exact)
+def _quotient_golden():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "make_fp8_quotient_blocks", os.path.join(GOLDEN, "make_fp8_quotient_blocks.py"))
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    return gen, json.load(open(os.path.join(GOLDEN, "fp8_quotient_blocks.json")))
+
+
+def quotient_golden_rows(blocks_per_row=8):
+    """The golden blocks as bf16 rows (blocks_per_row blocks of 128 channels,
+    the last row padded with zero blocks) with their expected codes and scales."""
+    _, g = _quotient_golden()
+    blocks = g["blocks"]
+    nrow = (len(blocks) + blocks_per_row - 1) // blocks_per_row
+    n = nrow * blocks_per_row
+    x = np.zeros((n, 128), np.uint16)
+    codes = np.zeros((n, 128), np.uint8)
+    scales = np.zeros(n, np.uint32)
+    for i, b in enumerate(blocks):
+        x[i] = b["bf16"]
+        codes[i] = b["codes"]
+        scales[i] = b["scale_bits"]
+    return (x.reshape(nrow, blocks_per_row * 128), codes.reshape(nrow, blocks_per_row * 128),
+            scales.reshape(nrow, blocks_per_row).view(np.float32), len(blocks))
+
+
+def test_fp8_quotient_golden_is_the_exact_definition():
+    """Every stored code and scale re-derived in exact rational arithmetic
+    (s = RNE32(amax/448), q = RNE32(x/s), E4M3 by torch's cast after the clamp),
+    and the blocks separate the definition from x*(448/amax) and x*(1/s)."""
+    gen, g = _quotient_golden()
+    n1 = n2 = 0
+    for b in g["blocks"]:
+        sbits, codes = gen.exact_block(b["bf16"][0], b["bf16"][1:])
+        assert sbits == b["scale_bits"] and codes == b["codes"]
+        a1, a2 = gen.alt_codes(b["bf16"][0], b["bf16"][1:])
+        assert a1 == b["codes_mul_448_over_amax"] and a2 == b["codes_mul_reciprocal"]
+        n1 += sum(c != d for c, d in zip(codes, a1))
+        n2 += sum(c != d for c, d in zip(codes, a2))
+    assert n1 >= 500 and n2 >= 500, (n1, n2)
+    # scales below 2^-100 and float32-subnormal scales are both present
+    sc = np.array([b["scale_bits"] for b in g["blocks"]], np.uint32).view(np.float32)
+    assert np.any((sc > 0) & (sc < 2.0 ** -100)) and np.any((sc > 0) & (sc < 2.0 ** -126))
+
+
+def test_fp8_quotient_golden_blocks():
+    """The oracle's fp8 dispatch reproduces the exactly derived codes and scales
+    of blocks where the float32 quotient decides the E4M3 code."""
+    x, codes, scales, _ = quotient_golden_rows()
+    T = x.shape[0]
+    idx = np.zeros((T, 1), np.int32)
+    lay = oracle.layout(idx, 1, 1, 1, 0)
+    q, sc = oracle.dispatch_fp8(x, lay, 1, 1, False)
+    bad = np.nonzero(q != codes)
+    assert bad[0].size == 0, (bad[0][:4], bad[1][:4], q[bad][:4], codes[bad][:4])
+    assert np.array_equal(sc.view(np.uint32), scales.view(np.uint32))
