@@ -227,26 +227,138 @@ def copy_ceiling(torch, dev, reps: int = 5) -> float:
     return 2 * CEILING_BYTES / (best * 1e-3) / 1e9
 
 
-def cpu_baseline(w, d, y_bits, relay=False, fp8=False, min_seconds=12.0, max_reps=64):
-    """The oracle as it stands (single-threaded C loops) on full layers of the
-    same workload: layout + dispatch (per-expert or relay, bf16 or fp8) +
-    combine of the same expert outputs the GPU combines, repeated until about
-    min_seconds of CPU time have been spent. Returns (seconds per layer,
-    layers timed)."""
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime this process already uses
+    (torch's), for the library's measurement hook (epx_time_next_call): the
+    events are bound to the library's kernels, so torch's own event objects,
+    which only know their own records, cannot read them."""
+
+    def __init__(self):
+        import ctypes
+        self._ct = ctypes
+        self._hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD)
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._events = []
+        self._free = []
+
+    def _new(self) -> int:
+        ev = self._ct.c_void_p()
+        if self._hip.hipEventCreate(self._ct.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self._events.append(ev.value)
+        return ev.value
+
+    def reserve(self, pairs: int):
+        """Create event pairs ahead of a timed loop, which then only takes them."""
+        self._free += [(self._new(), self._new()) for _ in range(pairs)]
+
+    def pair(self):
+        return self._free.pop() if self._free else (self._new(), self._new())
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = self._ct.c_float()
+        rc = self._hip.hipEventElapsedTime(self._ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc}): a timed call launched no kernel?")
+        return float(ms.value)
+
+    def release(self):
+        for e in self._events:
+            self._hip.hipEventDestroy(e)
+        self._events = []
+
+
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads() -> int:
+    """Host threads for the threaded baseline: the cores this process may
+    run on, at most 16 (one GPU's share of the host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_layer(w, d, y_bits, relay, fp8, pool=None, nthreads=1):
+    """One full layer through the oracle as it stands: layout (sequential),
+    dispatch and combine. With a pool, dispatch and combine run the same
+    oracle functions on nthreads contiguous token slices at once (ctypes
+    releases the GIL); every slice writes its own rows of the shared
+    outputs, so the result is the same bytes."""
     import oracle
     T, k = d["topk_idx"].shape
-    reps, t_total = 0, 0.0
-    while reps < max_reps and (t_total < min_seconds or reps < 2):
-        t0 = time.perf_counter()
-        lay = oracle.layout(d["topk_idx"], w.num_experts, w.num_ranks, w.num_hosts, w.my_rank, relay=relay)
+    H, hidden = w.num_hosts, d["x"].shape[1]
+    lay = oracle.layout(d["topk_idx"], w.num_experts, w.num_ranks, w.num_hosts, w.my_rank, relay=relay)
+    rows = int(lay["totals"][1] if relay else lay["totals"][0])
+    if pool is None:
         if fp8:
-            oracle.dispatch_fp8(d["x"], lay, k, w.num_hosts, relay)
+            oracle.dispatch_fp8(d["x"], lay, k, H, relay)
         else:
-            oracle.dispatch_bf16(d["x"], lay, k, w.num_hosts, relay)
-        oracle.combine(y_bits, lay, d["topk_weights"])
-        t_total += time.perf_counter() - t0
-        reps += 1
-    return t_total / reps, reps
+            oracle.dispatch_bf16(d["x"], lay, k, H, relay)
+        return oracle.combine(y_bits, lay, d["topk_weights"])
+    if fp8:
+        recv = (np.zeros((rows, hidden), np.uint8), np.zeros((rows, hidden // 128), np.float32))
+    else:
+        recv = np.zeros((rows, hidden), np.uint16)
+    out = np.zeros((T, hidden), np.uint16)
+    cuts = np.linspace(0, T, nthreads + 1).astype(int)
+    slices = [(int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+
+    def disp(sl):
+        a, b = sl
+        sub = {"slot": lay["slot"][a * k:b * k]}
+        if relay:
+            sub["relay_slot"] = lay["relay_slot"][a * H:b * H]
+        f = oracle.dispatch_fp8 if fp8 else oracle.dispatch_bf16
+        f(d["x"][a:b], sub, k, H, relay, rows=rows, out=recv)
+
+    def comb(sl):
+        a, b = sl
+        oracle.combine(y_bits, {"slot": lay["slot"][a * k:b * k]}, d["topk_weights"][a:b], out=out[a:b])
+
+    list(pool.map(disp, slices))
+    list(pool.map(comb, slices))
+    return out
+
+
+def cpu_baseline(w, d, y_bits, layer_bytes, relay=False, fp8=False, min_seconds=12.0, max_reps=64):
+    """The oracle as it stands on full layers of the same workload, on the
+    host of this GPU: single-threaded, then with dispatch and combine sharded
+    over the host's cores (cpu_layer); about min_seconds of CPU work in all.
+    Both runs give the same output bytes (checked)."""
+    from concurrent.futures import ThreadPoolExecutor
+    n = cpu_threads()
+
+    def timed(fn, budget):
+        reps, t_total, res = 0, 0.0, None
+        while reps < max_reps and (t_total < budget or reps < 2):
+            t0 = time.perf_counter()
+            res = fn()
+            t_total += time.perf_counter() - t0
+            reps += 1
+        return t_total / reps, reps, res
+
+    s1, r1, out1 = timed(lambda: cpu_layer(w, d, y_bits, relay, fp8), min_seconds * 0.6)
+    with ThreadPoolExecutor(max_workers=n) as pool:
+        sn, rn, outn = timed(lambda: cpu_layer(w, d, y_bits, relay, fp8, pool, n), min_seconds * 0.4)
+    assert np.array_equal(out1, outn), "threaded oracle layer differs from the single-threaded one"
+    what = f"layout + {'relay' if relay else 'per-expert'} {'fp8' if fp8 else 'bf16'} dispatch + combine"
+    return {"value": round(layer_bytes / sn / 1e9, 3), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "us_per_layer": round(sn * 1e6, 1),
+            "single_thread": {"value": round(layer_bytes / s1 / 1e9, 3), "us_per_layer": round(s1 * 1e6, 1),
+                              "layers": r1},
+            "cpu_model": host_cpu_model(),
+            "sample": f"{rn} full layers ({what}) of the {w.name} workload with dispatch and combine on "
+                      f"{n} token slices in {n} threads (layout sequential), beside {r1} single-threaded "
+                      f"layers; the C oracle unchanged"}
 
 
 def main(argv=None) -> int:
@@ -277,11 +389,13 @@ def main(argv=None) -> int:
                     help="also time layers captured in a HIP graph (16 per graph) and replayed: the "
                          "layer time without per-launch host overhead (default: on, except with "
                          "--swap-planner)")
-    ap.add_argument("--event-every", type=int, default=4, metavar="N",
-                    help="record the per-kernel HIP events on every N-th timed step (1: all)")
+    ap.add_argument("--event-every", type=int, default=1, metavar="N",
+                    help="arm the per-call kernel events on every N-th timed step (1: all)")
     ap.add_argument("--cold", action="store_true",
-                    help="read a 512 MiB scratch buffer before every step (evicts the 256 MB "
-                         "Infinity Cache and L2); per-kernel and layer times then exclude the flush")
+                    help="headline from cold steps: a 512 MiB scratch buffer read before every step "
+                         "(evicts the 256 MB Infinity Cache and L2; the flush is outside every "
+                         "timing). Either way the line also carries the other cache state's "
+                         "per-kernel times")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -310,6 +424,7 @@ def main(argv=None) -> int:
     import torch
     from combine_epx_get_amd import epx
     from combine_epx_get_amd import workloads as W
+    hipev = HipEvents()
 
     w = W.WORKLOADS[args.workload]
     mode = args.mode or ("relay" if args.relay_receive else w.modes[0])
@@ -374,52 +489,54 @@ def main(argv=None) -> int:
                     "host_bad": torch.empty(H, dtype=torch.int32, device=dev)}
         n_plans = [0]
 
-    def step(ev=None):
-        # launches go to the current stream (a capture stream under --graph)
+    def step(rec=None):
+        """One layer on the current stream (a capture stream under --graph).
+        With `rec` (a list), every library call first arms the measurement
+        hook with a fresh pair of HIP events, bound to the call's own
+        kernels, and (name, start, stop) is appended to rec."""
         stream = torch.cuda.current_stream()
 
-        def rec(i):
-            if ev is not None:
-                ev[i].record(stream)
+        def arm(name):
+            if rec is not None:
+                a, b = hipev.pair()
+                rec.append((name, a, b))
+                epx.epx_time_next_call(a, b)
 
-        rec(0)
         if fused:
-            # layout and dispatch in one call: its time is events 0 -> 1
+            arm("layout_dispatch")
             epx.epx_layout_dispatch(p, idx, L, x, out_dtype, recv, scales, stream)
-            rec(1)
         else:
+            arm("layout")
             epx.epx_get_layout(p, idx, L, stream)
-            rec(1)
         if planner:
             i = n_plans[0] % 2
             plan_out["slot_expert"] = places[1 - i]
+            arm("swap_planner")
             epx.epx_plan_swaps(E, R, H, L["expert_count"], places[i], args.swap_planner, plan_out, stream)
             n_plans[0] += 1
-        rec(6)
         if m > 1:
             # per-expert overlap order without the expert GEMMs: every group's
-            # dispatch, then every group's combine (events 7.. per launch)
+            # dispatch, then every group's combine
             for g in range(m):
+                arm(f"dispatch_g{g}")
                 epx.epx_dispatch_group(p, L, g, x, out_dtype, recv, scales, stream)
-                rec(7 + g)
-            rec(2)
             for g in range(m):
+                arm(f"combine_g{g}")
                 epx.epx_combine_group(p, L, g, y, wts, carry, out, stream)
-                rec(7 + m + g)
-            rec(3)
             return
         if not fused:
+            arm("dispatch")
             epx.epx_dispatch(p, L, x, out_dtype, recv, scales, stream)
-        rec(2)
         if receive:
+            arm("relay_fanout")
             epx.epx_relay_fanout(p, L, recv, fan, scales, fan_sc, stream)
-            rec(4)
+            arm("relay_partials")
             epx.epx_combine_relay_partials(p, L, y, wts, part, stream)
-            rec(5)
+            arm("relay_finish")
             epx.epx_combine_relay_finish(p, L, part, out, stream)
         else:
+            arm("combine")
             epx.epx_combine(p, L, y, wts, out, stream)
-        rec(3)
 
     if args.copy_calibration:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give
@@ -431,39 +548,49 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    # --cold: read a 512 MiB buffer before each step. Reading (not writing)
-    # leaves clean lines in the caches, so the dirty lines of the previous
-    # step are written back during the flush and none is left for the next
-    # kernel to write back inside its own time.
-    scratch = torch.ones(EVICT_BYTES // 4, dtype=torch.int32, device=dev) if args.cold else None
+    # Cold steps read a 512 MiB buffer first. Reading (not writing) leaves
+    # clean lines in the caches, so the dirty lines of the previous step are
+    # written back during the flush and none is left for the next kernel to
+    # write back inside its own time. The flush is outside every timing.
+    scratch = torch.ones(EVICT_BYTES // 4, dtype=torch.int32, device=dev)
 
-    def flush(i):
-        if scratch is not None:
-            scratch.max()
+    def flush():
+        scratch.max()
 
-    for i in range(args.warmup):
-        flush(i)
+    for _ in range(args.warmup):
+        if args.cold:
+            flush()
         step()
     torch.cuda.synchronize()
     assert epx.epx_read_error(L) == 0
     totals = L["totals"].cpu().numpy()
     rows = int(totals[1] if relay else totals[0])
 
-    # Per-kernel events on every step would slow the step they measure (each
-    # record is a marker the stream waits for: about 17 µs per large-batch
-    # step), so they are recorded on the last step of every `event_every`
-    # timed steps only (never on the first, which starts on an idle queue);
-    # the other steps run as a caller would run them.
-    every = max(1, min(args.event_every, args.steps))
-    timed = [i for i in range(args.steps) if i % every == every - 1]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7 + 2 * m)] for _ in timed]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        flush(i)
-        step(evs[i // every] if i % every == every - 1 else None)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    calls_per_step = (1 + (1 if planner else 0) +
+                      (2 * m if m > 1 else (0 if fused else 1) + (3 if receive else 1)))
+
+    def timed_steps(n, cold):
+        """n steps, the kernel events armed on every `event_every`-th one.
+        Returns (wall seconds, [records of the timed steps])."""
+        every = max(1, min(args.event_every, n))
+        recs = []
+        hipev.reserve((n // every) * calls_per_step)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            if cold:
+                flush()
+            r = [] if i % every == every - 1 else None
+            step(r)
+            if r is not None:
+                recs.append(r)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, recs
+
+    wall, recs = timed_steps(args.steps, args.cold)
+    # the other cache state, for the same kernels: cold steps (flush before
+    # each) beside a warm headline, warm steps beside a cold one
+    _, recs_other = timed_steps(args.steps, not args.cold)
     del scratch
 
     graph_us = None
@@ -509,21 +636,6 @@ def main(argv=None) -> int:
                 epx.epx_combine(p, L, y, wts, out, stream)
             graph_fused_us = time_graph(fused_layer)
 
-    lay_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    plan_ms = np.array([e[1].elapsed_time(e[6]) for e in evs])
-    dis_ms = np.array([e[6].elapsed_time(e[2]) for e in evs])
-    if receive:
-        fan_ms = np.array([e[2].elapsed_time(e[4]) for e in evs])
-        par_ms = np.array([e[4].elapsed_time(e[5]) for e in evs])
-        fin_ms = np.array([e[5].elapsed_time(e[3]) for e in evs])
-        com_ms = par_ms + fin_ms
-    else:
-        com_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
-    # the flush is not part of the layer: under --cold the step time comes
-    # from the events around the layer, otherwise from the wall clock
-    ms_per_step = float(step_ms.mean()) if args.cold else wall * 1e3 / args.steps
-
     nbytes = algorithmic_bytes(T, k, w.num_hosts, hidden, rows, relay, fp8)
     if receive:
         nbytes.update(relay_receive_bytes(T, k, w.num_hosts, hidden, rows, fp8, args.partials == "f32"))
@@ -531,44 +643,44 @@ def main(argv=None) -> int:
     if m > 1:
         nbytes = {"layout": nbytes["layout"],
                   **group_bytes(d["topk_idx"], w.num_experts, w.num_ranks, m, hidden, fp8)}
-    layer_bytes = sum(nbytes.values())
-    us_layer = float(step_ms.mean() * 1e3)
-    value = layer_bytes / (ms_per_step * 1e-3) / 1e9
-
-    def kern(ms, nb):
-        """Event times of one kernel over the timed steps (µs): mean (the
-        roofline's figure), median, min and max."""
-        us = np.asarray(ms, dtype=np.float64) * 1e3
-        return {"us": float(us.mean()), "us_median": float(np.median(us)), "us_min": float(us.min()),
-                "us_max": float(us.max()), "bytes": nb}
-
     if fused:
-        per_kernel = {"layout_dispatch": kern(lay_ms, nbytes["layout"] + nbytes["dispatch"])}
-    else:
-        per_kernel = {"layout": kern(lay_ms, nbytes["layout"])}
-    if m == 1 and not fused:
-        per_kernel["dispatch"] = kern(dis_ms, nbytes["dispatch"])
-    if m > 1:
-        for g in range(m):
-            d0 = 6 if g == 0 else 7 + g - 1
-            c0 = 2 if g == 0 else 7 + m + g - 1
-            per_kernel[f"dispatch_g{g}"] = kern([e[d0].elapsed_time(e[7 + g]) for e in evs],
-                                                nbytes[f"dispatch_g{g}"])
-            per_kernel[f"combine_g{g}"] = kern([e[c0].elapsed_time(e[7 + m + g]) for e in evs],
-                                               nbytes[f"combine_g{g}"])
+        nbytes = {"layout_dispatch": nbytes["layout"] + nbytes["dispatch"],
+                  **{n: v for n, v in nbytes.items() if n not in ("layout", "dispatch")}}
     if planner:
         # counts and placement in, placement, loads, pair records and flags out
         npair = H * ((R // H) // 2)
-        per_kernel["swap_planner"] = kern(plan_ms, 4 * (3 * E + 2 * R + 7 * npair + H))
-    if receive:
-        per_kernel["relay_fanout"] = kern(fan_ms, nbytes["relay_fanout"])
-        per_kernel["relay_partials"] = kern(par_ms, nbytes["relay_partials"])
-        per_kernel["relay_finish"] = kern(fin_ms, nbytes["relay_finish"])
-    elif m == 1:
-        per_kernel["combine"] = kern(com_ms, nbytes["combine"])
-    for v in per_kernel.values():
-        v["GBs"] = v["bytes"] / (v["us"] * 1e-6) / 1e9
-        v["frac_peak"] = v["GBs"] / PEAK_HBM_GBS
+        nbytes["swap_planner"] = 4 * (3 * E + 2 * R + 7 * npair + H)
+    layer_bytes = sum(v for n, v in nbytes.items() if n != "swap_planner")
+
+    def kernel_times(records):
+        """Per call: µs of its kernels (mean, median, min, max), bytes, GB/s
+        and fraction of peak; and the layer µs (first kernel's start to the
+        last kernel's end) of every timed step."""
+        per, layer = {}, []
+        for r in records:
+            for name, a, b in r:
+                per.setdefault(name, []).append(hipev.elapsed_ms(a, b) * 1e3)
+            layer.append(hipev.elapsed_ms(r[0][1], r[-1][2]) * 1e3)
+        out = {}
+        for name, us in per.items():
+            us = np.asarray(us, dtype=np.float64)
+            nb = nbytes[name]
+            v = {"us": float(us.mean()), "us_median": float(np.median(us)), "us_min": float(us.min()),
+                 "us_max": float(us.max()), "bytes": nb}
+            v["GBs"] = nb / (v["us"] * 1e-6) / 1e9
+            v["frac_peak"] = v["GBs"] / PEAK_HBM_GBS
+            out[name] = v
+        return out, np.asarray(layer, dtype=np.float64)
+
+    per_kernel, layer_us = kernel_times(recs)
+    other_kernel, other_layer_us = kernel_times(recs_other)
+    hipev.release()
+    # the flush is not part of the layer: cold steps take their time from the
+    # kernel events, warm steps from the wall clock
+    ms_per_step = float(layer_us.mean() / 1e3) if args.cold else wall * 1e3 / args.steps
+    us_layer = float(layer_us.mean())
+    value = layer_bytes / (ms_per_step * 1e-3) / 1e9
+
     dom = max((n for n in per_kernel if n not in ("layout", "swap_planner")), key=lambda n: per_kernel[n]["us"])
     kname = {"dispatch": "dispatch_fp8_kernel" if fp8 else "dispatch_bf16_kernel",
              "combine": "combine_kernel", "relay_fanout": "relay_fanout_kernel",
@@ -582,15 +694,22 @@ def main(argv=None) -> int:
                 "achieved": round(per_kernel[dom]["GBs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(per_kernel[dom]["frac_peak"], 4), "traffic": traffic,
                 "algorithmic_bytes": per_kernel[dom]["bytes"],
+                "timing": "HIP events bound to the kernels' dispatch packets (hipExtLaunchKernel)",
                 "copy_ceiling_GBs": round(copy_ceiling(torch, dev), 1)}
+
+    def rounded(pk):
+        return {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                for n, v in pk.items()}
+
+    other = {"cache": "warm (back-to-back steps)" if args.cold else
+             "cold (512 MiB scratch read before each step)",
+             "us_per_layer": round(float(other_layer_us.mean()), 2),
+             "kernels": {n: {"us": round(v["us"], 3), "frac_peak": round(v["frac_peak"], 4)}
+                         for n, v in other_kernel.items()}}
 
     cpu = None
     if args.cpu_seconds > 0 and not receive and m == 1:
-        cpu_s, reps = cpu_baseline(w, d, y_np, relay, fp8, args.cpu_seconds)
-        cpu = {"value": round(layer_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "us_per_layer": round(cpu_s * 1e6, 1),
-               "sample": f"{reps} full layers (layout + {mode.replace('_', '-')} {dtype} dispatch + combine) "
-                         f"of the {args.workload} workload, single-threaded C oracle"}
+        cpu = cpu_baseline(w, d, y_np, layer_bytes, relay, fp8, args.cpu_seconds)
 
     line = {
         "metric": "dispatch+combine µs/layer and HBM GB/s (% of MI355X peak) at 4096 tok, h=7168",
@@ -608,13 +727,13 @@ def main(argv=None) -> int:
                    **({"expert_groups": m} if m > 1 else {}),
                    **({"fused_layout_dispatch": True} if fused else {})},
         "cache": "cold (512 MiB scratch read before each step)" if args.cold else "warm (back-to-back steps)",
-        "event_every": every,
+        "event_every": max(1, min(args.event_every, args.steps)),
         "us_per_layer": round(us_layer, 2),
         **({"us_per_layer_graph": round(graph_us, 2)} if graph_us is not None else {}),
         **({"us_per_layer_graph_fused": round(graph_fused_us, 2)} if graph_fused_us is not None else {}),
         "pct_of_peak_layer": round(100 * layer_bytes / (us_layer * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
-        "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                    for n, v in per_kernel.items()},
+        "kernels": rounded(per_kernel),
+        "cold" if not args.cold else "warm": other,
         "layer_bytes": layer_bytes, "rows": rows,
         "imbalance_ratio": round(float(totals[2]) / (T * k / w.num_experts), 3),
         "roofline": roofline,

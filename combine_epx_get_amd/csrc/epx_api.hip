@@ -5,9 +5,23 @@
 
 #include "epx_internal.h"
 
+namespace epx {
+TimingHook &timing_hook()
+{
+    static thread_local TimingHook hook;
+    return hook;
+}
+}  // namespace epx
+
 namespace {
 
 using epx::Geometry;
+
+// Clears the measurement hook when an entry point returns, whatever it did:
+// the hook applies to one call.
+struct HookScope {
+    ~HookScope() { epx::timing_hook() = epx::TimingHook{}; }
+};
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -185,6 +199,14 @@ extern "C" {
 
 int32_t epx_abi_version(void) { return EPX_ABI_VERSION; }
 
+epx_status epx_time_next_call(void *start_event, void *stop_event)
+{
+    if ((start_event == nullptr) != (stop_event == nullptr))
+        return EPX_ERR_ARG;
+    epx::timing_hook() = epx::TimingHook{(hipEvent_t)start_event, (hipEvent_t)stop_event};
+    return EPX_OK;
+}
+
 const char *epx_status_string(epx_status s)
 {
     switch (s) {
@@ -204,6 +226,7 @@ const char *epx_status_string(epx_status s)
 
 epx_status epx_layout_sizes(const epx_problem *p, int64_t sizes_out[EPX_LAYOUT_NARRAYS])
 {
+    HookScope hook_scope;
     Geometry g;
     epx_status st = make_geometry(p, &g);
     if (st != EPX_OK)
@@ -217,6 +240,7 @@ epx_status epx_layout_sizes(const epx_problem *p, int64_t sizes_out[EPX_LAYOUT_N
 epx_status epx_get_layout(const epx_problem *p, const int32_t *topk_idx, const epx_layout *layout,
                           void *stream)
 {
+    HookScope hook_scope;
     Geometry g;
     epx_status st = make_geometry(p, &g);
     if (st != EPX_OK)
@@ -232,6 +256,7 @@ epx_status epx_dispatch(const epx_problem *p, const epx_layout *layout, const vo
                         int32_t hidden, int32_t out_dtype, void *recv, float *recv_scales,
                         int64_t capacity_rows, void *stream)
 {
+    HookScope hook_scope;
     return dispatch_impl(p, layout, -1, x, hidden, out_dtype, recv, recv_scales, capacity_rows,
                          stream);
 }
@@ -241,6 +266,7 @@ epx_status epx_layout_dispatch(const epx_problem *p, const int32_t *topk_idx,
                                int32_t out_dtype, void *recv, float *recv_scales,
                                int64_t capacity_rows, void *stream)
 {
+    HookScope hook_scope;
     Geometry g;
     epx_status st = make_geometry(p, &g);
     if (st != EPX_OK)
@@ -271,6 +297,7 @@ epx_status epx_dispatch_group(const epx_problem *p, const epx_layout *layout, in
                               const void *x, int32_t hidden, int32_t out_dtype, void *recv,
                               float *recv_scales, int64_t capacity_rows, void *stream)
 {
+    HookScope hook_scope;
     if (group < 0)
         return EPX_ERR_ARG;
     return dispatch_impl(p, layout, group, x, hidden, out_dtype, recv, recv_scales, capacity_rows,
@@ -281,6 +308,7 @@ epx_status epx_combine(const epx_problem *p, const epx_layout *layout, const voi
                        int64_t y_rows, const float *topk_weights, int32_t hidden, void *out,
                        void *stream)
 {
+    HookScope hook_scope;
     return combine_impl(p, layout, -1, y, y_rows, topk_weights, hidden, nullptr, out, stream);
 }
 
@@ -288,6 +316,7 @@ epx_status epx_combine_group(const epx_problem *p, const epx_layout *layout, int
                              const void *y, int64_t y_rows, const float *topk_weights,
                              int32_t hidden, float *carry, void *out, void *stream)
 {
+    HookScope hook_scope;
     if (group < 0)
         return EPX_ERR_ARG;
     return combine_impl(p, layout, group, y, y_rows, topk_weights, hidden, carry, out, stream);
@@ -298,6 +327,7 @@ epx_status epx_relay_fanout(const epx_problem *p, const epx_layout *layout,
                             int64_t relay_capacity_rows, int32_t hidden, int32_t dtype,
                             void *recv, float *recv_scales, int64_t capacity_rows, void *stream)
 {
+    HookScope hook_scope;
     Geometry g;
     epx_status st = make_geometry(p, &g);
     if (st != EPX_OK)
@@ -330,6 +360,7 @@ epx_status epx_combine_relay_partials(const epx_problem *p, const epx_layout *la
                                       int32_t hidden, int32_t partial_dtype, void *partials,
                                       int64_t partial_capacity_rows, void *stream)
 {
+    HookScope hook_scope;
     Geometry g;
     epx_status st = make_geometry(p, &g);
     if (st != EPX_OK)
@@ -356,6 +387,7 @@ epx_status epx_combine_relay_finish(const epx_problem *p, const epx_layout *layo
                                     const void *partials, int64_t partial_capacity_rows,
                                     int32_t partial_dtype, int32_t hidden, void *out, void *stream)
 {
+    HookScope hook_scope;
     Geometry g;
     epx_status st = make_geometry(p, &g);
     if (st != EPX_OK)
@@ -378,6 +410,7 @@ epx_status epx_combine_relay_finish(const epx_problem *p, const epx_layout *layo
 
 epx_status epx_read_error(const epx_layout *layout, int32_t *bad_count, void *stream)
 {
+    HookScope hook_scope;
     if (!layout || !layout->totals)
         return EPX_ERR_ARG;
     int32_t totals[4];
@@ -397,6 +430,7 @@ epx_status epx_plan_swaps(int32_t num_experts, int32_t num_ranks, int32_t num_ho
                           int32_t *rank_load_after, int32_t *swaps, int32_t *host_bad,
                           void *stream)
 {
+    HookScope hook_scope;
     const int32_t E = num_experts, R = num_ranks, H = num_hosts;
     if (E < 1 || E > epx::kMaxExperts || R < 1 || H < 1 || H > epx::kMaxHosts || E % R != 0 ||
         R % H != 0 || R / H > epx::kMaxRanksPerHost || tau < 0)
@@ -417,6 +451,7 @@ epx_status epx_plan_swaps(int32_t num_experts, int32_t num_ranks, int32_t num_ho
 
 epx_status epx_f32_to_e4m3(const float *in, uint8_t *out, int64_t n, void *stream)
 {
+    HookScope hook_scope;
     if (n < 0 || (n > 0 && (!in || !out || !aligned(in, 4))))
         return EPX_ERR_ARG;
     if (n == 0)

@@ -174,7 +174,7 @@ hipError_t launch_plan_swaps(int E, int R, int H, const int32_t *count, const in
 {
     const int epr = E / R, rph = R / H;
     const size_t lds = ((size_t)E + 2 * (size_t)rph * epr) * sizeof(int32_t);
-    hipLaunchKernelGGL(plan_swaps_kernel, dim3(H), dim3(kThreads), lds, stream, E, epr, rph, count,
+    launch(plan_swaps_kernel, dim3(H), dim3(kThreads), lds, stream, E, epr, rph, count,
                        slot_in, tau, slot_out, load_before, load_after, swaps, host_bad);
     return hipGetLastError();
 }

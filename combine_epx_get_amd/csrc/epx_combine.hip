@@ -224,7 +224,7 @@ hipError_t launch_combine_group(const Geometry &g, const epx_layout &L, int grou
     int slice, threads;
     combine_shape(g, nvec, kChunks, slice, threads);
     const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
-    hipLaunchKernelGGL(combine_group_kernel, grid, dim3(threads), 0, stream, (const u32x4 *)y,
+    launch(combine_group_kernel, grid, dim3(threads), 0, stream, (const u32x4 *)y,
                        nvec, slice, (const int32_t *)L.slot, w, g.k,
                        (const int32_t *)L.group_offset + group * g.R,
                        (const int32_t *)L.group_offset + (group + 1) * g.R, (float4 *)carry,
@@ -245,11 +245,11 @@ hipError_t launch_combine(const Geometry &g, const epx_layout &L, const void *y,
     combine_shape(g, nvec, chunks, slice, threads);
     const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
     if (chunks == 1)
-        hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(threads), 0, stream, (const u32x4 *)y,
+        launch(combine_kernel<1>, grid, dim3(threads), 0, stream, (const u32x4 *)y,
                            nvec, slice, (const int32_t *)L.slot, w, g.k, (u32x4 *)out,
                            (const int32_t *)L.totals, (int64_t)g.T);
     else
-        hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(threads), 0, stream, (const u32x4 *)y,
+        launch(combine_kernel<2>, grid, dim3(threads), 0, stream, (const u32x4 *)y,
                            nvec, slice, (const int32_t *)L.slot, w, g.k, (u32x4 *)out,
                            (const int32_t *)L.totals, (int64_t)g.T);
     return hipGetLastError();

@@ -174,7 +174,7 @@ hipError_t launch_dispatch_bf16(const Geometry &g, const epx_layout &L, const vo
     const int nvec = hidden / 8;
     const int slice = slice_width(g.T, nvec, kWave, 1 << 30, 2048);
     const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
-    hipLaunchKernelGGL(dispatch_bf16_kernel, grid, dim3(kThreads), 0, stream, (const u32x4 *)x,
+    launch(dispatch_bf16_kernel, grid, dim3(kThreads), 0, stream, (const u32x4 *)x,
                        nvec, slice, dest, D, (u32x4 *)recv, (const int32_t *)L.totals, lo_p,
                        hi_p, (int64_t)g.T);
     return hipGetLastError();
@@ -198,7 +198,7 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const epx_layout &L, const voi
     const int slice = slice_width(g.T, nvec, 16, kMaxSliceVec, 2048 * rows_per_token);
     const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
     const size_t lds = (size_t)slice * 8 + (size_t)(slice / 16) * sizeof(float);
-    hipLaunchKernelGGL(dispatch_fp8_kernel, grid, dim3(kThreads), lds, stream, (const u32x4 *)x,
+    launch(dispatch_fp8_kernel, grid, dim3(kThreads), lds, stream, (const u32x4 *)x,
                        nvec, slice, dest, D, (uint8_t *)recv, scales, (const int32_t *)L.totals,
                        lo_p, hi_p, (int64_t)g.T);
     return hipGetLastError();
@@ -207,7 +207,7 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const epx_layout &L, const voi
 hipError_t launch_f32_to_e4m3(const float *in, uint8_t *out, int64_t n, hipStream_t stream)
 {
     const int64_t blocks = (n + 255) / 256;
-    hipLaunchKernelGGL(f32_to_e4m3_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)),
+    launch(f32_to_e4m3_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)),
                        dim3(256), 0, stream, in, out, n);
     return hipGetLastError();
 }

@@ -457,10 +457,10 @@ bool launch_layout_dispatch(const Geometry &g, const int32_t *idx, const epx_lay
         return false;
     const dim3 grid = item_grid((int64_t)g.T + 1, (nvec + slice - 1) / slice);
     if (fp8)
-        hipLaunchKernelGGL(layout_dispatch_kernel<true>, grid, dim3(kFThreads), lds, stream, idx, g,
+        launch(layout_dispatch_kernel<true>, grid, dim3(kFThreads), lds, stream, idx, g,
                            L, (const u32x4 *)x, nvec, slice, recv, scales);
     else
-        hipLaunchKernelGGL(layout_dispatch_kernel<false>, grid, dim3(kFThreads), lds, stream, idx,
+        launch(layout_dispatch_kernel<false>, grid, dim3(kFThreads), lds, stream, idx,
                            g, L, (const u32x4 *)x, nvec, slice, recv, scales);
     *err = hipGetLastError();
     return true;

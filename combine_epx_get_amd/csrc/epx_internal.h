@@ -2,6 +2,7 @@
 // Not installed; the public interface is include/epx.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -69,6 +70,35 @@ __device__ __forceinline__ int64_t item_index()
 // 16-byte and 8-byte native vectors (global_load/store_dwordx4, dwordx2).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Measurement hook (epx_time_next_call): HIP events that the next library
+// call made from this host thread binds to its kernels' dispatch packets --
+// `start` to the first kernel it launches, `stop` to every kernel, so that
+// it ends up marking the last one's end. Every entry point clears the hook
+// when it returns.
+struct TimingHook {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+TimingHook &timing_hook();
+
+// Every kernel launch of the library. With no hook armed it is the plain
+// launch; with one, the launch carries the hook's events
+// (hipExtLaunchKernel), which time the kernel alone, as a profiler does.
+// The caller reads the launch status with hipGetLastError().
+template <typename... KArgs, typename... Args>
+inline void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
+                   hipStream_t stream, Args... args)
+{
+    TimingHook &h = timing_hook();
+    if (h.stop == nullptr) {
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+        return;
+    }
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, stream, h.start, h.stop, 0u,
+                          args...);
+    h.start = nullptr;
+}
 
 // Launchers (each returns the launch status).
 hipError_t launch_layout(const Geometry &g, const int32_t *idx, const epx_layout &L,

@@ -825,7 +825,7 @@ hipError_t launch_count(const Geometry &g, const int32_t *idx, const epx_layout 
 {
     const int ncol = g.E + g.R + g.H + 1;
     const size_t lds = (size_t)(ncol + 3 * g.ct * g.k) * sizeof(int32_t);
-    hipLaunchKernelGGL(layout_count_kernel, dim3(g.G), dim3(kCountThreads), lds, stream, idx, g,
+    launch(layout_count_kernel, dim3(g.G), dim3(kCountThreads), lds, stream, idx, g,
                        L.workspace);
     return hipGetLastError();
 }
@@ -834,7 +834,7 @@ hipError_t launch_scan(const Geometry &g, const epx_layout &L, hipStream_t strea
 {
     const int ncol = g.E + g.R + g.H + 1;
     const int cols_per_block = 256 / kWave;
-    hipLaunchKernelGGL(layout_scan_kernel, dim3((ncol + cols_per_block - 1) / cols_per_block),
+    launch(layout_scan_kernel, dim3((ncol + cols_per_block - 1) / cols_per_block),
                        dim3(256), 0, stream, g, L.workspace);
     return hipGetLastError();
 }
@@ -846,7 +846,7 @@ hipError_t launch_layout(const Geometry &g, const int32_t *idx, const epx_layout
 {
     const size_t small = small_layout_lds(g);
     if (small > 0) {
-        hipLaunchKernelGGL(layout_small_kernel, dim3(1), dim3(kSmallThreads), small, stream, idx,
+        launch(layout_small_kernel, dim3(1), dim3(kSmallThreads), small, stream, idx,
                            g, L);
         return hipGetLastError();
     }
@@ -856,13 +856,13 @@ hipError_t launch_layout(const Geometry &g, const int32_t *idx, const epx_layout
     int nww = 0;
     const size_t lds_assign = assign_lds(g, kAssignThreads, nww);
     if (g.G <= kSumsMaxG) {
-        hipLaunchKernelGGL(layout_assign_kernel<true>, dim3(g.G), dim3(kAssignThreads), lds_assign,
+        launch(layout_assign_kernel<true>, dim3(g.G), dim3(kAssignThreads), lds_assign,
                            stream, idx, g, (const int32_t *)L.workspace, L, nww);
         return hipGetLastError();
     }
     if ((err = launch_scan(g, L, stream)) != hipSuccess)
         return err;
-    hipLaunchKernelGGL(layout_assign_kernel<false>, dim3(g.G), dim3(kAssignThreads), lds_assign,
+    launch(layout_assign_kernel<false>, dim3(g.G), dim3(kAssignThreads), lds_assign,
                        stream, idx, g, (const int32_t *)L.workspace, L, nww);
     return hipGetLastError();
 }
@@ -897,11 +897,11 @@ bool launch_layout_assign_dispatch(const Geometry &g, const int32_t *idx, const 
         return true;
     const dim3 grid = item_grid((int64_t)g.G + g.T, (nvec + slice - 1) / slice);
     if (fp8)
-        hipLaunchKernelGGL(assign_copy_kernel<true>, grid, dim3(kFusedThreads), lds, stream, idx, g,
+        launch(assign_copy_kernel<true>, grid, dim3(kFusedThreads), lds, stream, idx, g,
                            (const int32_t *)L.workspace, L, nww, (const u32x4 *)x, nvec, slice,
                            recv, scales);
     else
-        hipLaunchKernelGGL(assign_copy_kernel<false>, grid, dim3(kFusedThreads), lds, stream, idx,
+        launch(assign_copy_kernel<false>, grid, dim3(kFusedThreads), lds, stream, idx,
                            g, (const int32_t *)L.workspace, L, nww, (const u32x4 *)x, nvec, slice,
                            recv, scales);
     *err = hipGetLastError();

@@ -296,7 +296,7 @@ hipError_t launch_relay_fanout(const Geometry &g, const epx_layout &L, const voi
     const int row_vec = (int)(row_bytes / 16);
     const int slice = slices_for(cap, row_vec, kWave, 2048);
     const dim3 grid = item_grid(cap, (row_vec + slice - 1) / slice);
-    hipLaunchKernelGGL(relay_fanout_kernel, grid, dim3(kThreads), 0, stream,
+    launch(relay_fanout_kernel, grid, dim3(kThreads), 0, stream,
                        (const u32x4 *)relay_rows, relay_scales, row_vec, nsc, slice, g.k, L,
                        (u32x4 *)recv, recv_scales);
     return hipGetLastError();
@@ -311,10 +311,10 @@ hipError_t launch_relay_partials(const Geometry &g, const epx_layout &L, const v
     const int slice = slices_for(cap, nvec, kWave, 2048);
     const dim3 grid = item_grid(cap, (nvec + slice - 1) / slice);
     if (bf16_out)
-        hipLaunchKernelGGL(relay_partials_kernel<true>, grid, dim3(kThreads), 0, stream,
+        launch(relay_partials_kernel<true>, grid, dim3(kThreads), 0, stream,
                            (const u32x4 *)y, nvec, slice, w, g.k, L, partials);
     else
-        hipLaunchKernelGGL(relay_partials_kernel<false>, grid, dim3(kThreads), 0, stream,
+        launch(relay_partials_kernel<false>, grid, dim3(kThreads), 0, stream,
                            (const u32x4 *)y, nvec, slice, w, g.k, L, partials);
     return hipGetLastError();
 }
@@ -326,10 +326,10 @@ hipError_t launch_relay_finish(const Geometry &g, const epx_layout &L, const voi
     const int slice = slices_for(g.T, nvec, kWave, 2048);
     const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
     if (bf16_in)
-        hipLaunchKernelGGL(relay_finish_kernel<true>, grid, dim3(kThreads), 0, stream, partials,
+        launch(relay_finish_kernel<true>, grid, dim3(kThreads), 0, stream, partials,
                            nvec, slice, g.H, L, (u32x4 *)out, (int64_t)g.T);
     else
-        hipLaunchKernelGGL(relay_finish_kernel<false>, grid, dim3(kThreads), 0, stream, partials,
+        launch(relay_finish_kernel<false>, grid, dim3(kThreads), 0, stream, partials,
                            nvec, slice, g.H, L, (u32x4 *)out, (int64_t)g.T);
     return hipGetLastError();
 }

@@ -70,12 +70,13 @@ _lib.epx_combine_group.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(e
                                    _P, ctypes.c_int64, _P, ctypes.c_int32, _P, _P, _P]
 _lib.epx_plan_swaps.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32,
                                 _P, _P, _P, _P, _P, _P]
+_lib.epx_time_next_call.argtypes = [_P, _P]
 _lib.epx_status_string.argtypes = [ctypes.c_int]
 _lib.epx_status_string.restype = ctypes.c_char_p
 for _f in ("epx_layout_sizes", "epx_get_layout", "epx_dispatch", "epx_combine", "epx_read_error",
            "epx_f32_to_e4m3", "epx_relay_fanout", "epx_combine_relay_partials",
            "epx_combine_relay_finish", "epx_plan_swaps", "epx_dispatch_group", "epx_combine_group",
-           "epx_layout_dispatch"):
+           "epx_layout_dispatch", "epx_time_next_call"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.epx_abi_version.restype = ctypes.c_int32
 NARRAYS = len(LAYOUT_FIELDS)
@@ -256,6 +257,13 @@ def epx_read_error(layout: Layout, stream=None) -> int:
     if code not in (0, 2):
         _check(code, "epx_read_error")
     return int(bad.value)
+
+
+def epx_time_next_call(start_event: Optional[int], stop_event: Optional[int]) -> None:
+    """Bind two raw hipEvent_t handles to the kernels of the next library call
+    from this thread (start: its first kernel's start, stop: its last kernel's
+    end); None, None disarms."""
+    _check(_lib.epx_time_next_call(start_event, stop_event), "epx_time_next_call")
 
 
 def epx_f32_to_e4m3(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:

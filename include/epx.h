@@ -329,6 +329,19 @@ EPX_API epx_status epx_read_error(const epx_layout *layout, int32_t *bad_count, 
  * point for checking the conversion exhaustively. */
 EPX_API epx_status epx_f32_to_e4m3(const float *in, uint8_t *out, int64_t n, void *stream);
 
+/* Measurement hook. The kernels that the next library call made from this
+ * host thread launches carry the two HIP events (hipEvent_t, created by the
+ * caller with timing enabled) on their own dispatch packets
+ * (hipExtLaunchKernel): `start_event` is recorded when that call's first
+ * kernel begins and `stop_event` when its last kernel ends, so
+ * hipEventElapsedTime gives the call's kernel time without the gaps that
+ * event records placed around the call add. The hook applies to one call,
+ * whatever it returns, and is cleared when that call returns; a call that
+ * launches nothing (an error, an empty batch) leaves the events unrecorded.
+ * Both NULL disarms it. Errors: EPX_ERR_ARG if exactly one is NULL. For
+ * benchmarks and profiling; it changes no result. */
+EPX_API epx_status epx_time_next_call(void *start_event, void *stop_event);
+
 EPX_API const char *epx_status_string(epx_status s);
 EPX_API int32_t epx_abi_version(void);
 

@@ -150,14 +150,17 @@ def layout(topk_idx: np.ndarray, num_experts: int, num_ranks: int, num_hosts: in
 
 
 def dispatch_bf16(x_bits: np.ndarray, lay: dict, topk: int, num_hosts: int, relay: bool,
-                  rows: Optional[int] = None, lib=None) -> np.ndarray:
-    """recv rows (uint16 bf16 bits) for per-expert or relay mode."""
+                  rows: Optional[int] = None, lib=None, out: Optional[np.ndarray] = None) -> np.ndarray:
+    """recv rows (uint16 bf16 bits) for per-expert or relay mode. With `out`
+    (a C-contiguous uint16 [rows, h] array) the rows are written there: x and
+    the slot arrays may then be a slice of the tokens, whose rows are still
+    addressed by the full layout's row numbers."""
     lib = lib or load()
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
     T, hidden = x.shape
     if rows is None:
         rows = int(lay["totals"][1] if relay else lay["totals"][0])
-    recv = np.zeros((max(rows, 0), hidden), np.uint16)
+    recv = np.zeros((max(rows, 0), hidden), np.uint16) if out is None else out
     slot = lay["slot"]
     rslot = lay.get("relay_slot", np.zeros(1, np.int32)) if relay else np.zeros(1, np.int32)
     rc = lib.oracle_dispatch_bf16(T, topk, num_hosts, int(relay), hidden, _p(slot), _p(rslot),
@@ -168,15 +171,19 @@ def dispatch_bf16(x_bits: np.ndarray, lay: dict, topk: int, num_hosts: int, rela
 
 
 def dispatch_fp8(x_bits: np.ndarray, lay: dict, topk: int, num_hosts: int, relay: bool,
-                 rows: Optional[int] = None, lib=None):
-    """(codes uint8 [rows, h], scales float32 [rows, h/128])."""
+                 rows: Optional[int] = None, lib=None, out=None):
+    """(codes uint8 [rows, h], scales float32 [rows, h/128]). With `out` =
+    (codes, scales) arrays the rows are written there (as dispatch_bf16)."""
     lib = lib or load()
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
     T, hidden = x.shape
     if rows is None:
         rows = int(lay["totals"][1] if relay else lay["totals"][0])
-    q = np.zeros((rows, hidden), np.uint8)
-    sc = np.zeros((rows, hidden // 128), np.float32)
+    if out is None:
+        q = np.zeros((rows, hidden), np.uint8)
+        sc = np.zeros((rows, hidden // 128), np.float32)
+    else:
+        q, sc = out
     slot = lay["slot"]
     rslot = lay.get("relay_slot", np.zeros(1, np.int32)) if relay else np.zeros(1, np.int32)
     rc = lib.oracle_dispatch_fp8(T, topk, num_hosts, int(relay), hidden, _p(slot), _p(rslot),
@@ -186,14 +193,19 @@ def dispatch_fp8(x_bits: np.ndarray, lay: dict, topk: int, num_hosts: int, relay
     return q, sc
 
 
-def combine(y_bits: np.ndarray, lay: dict, topk_weights: np.ndarray, lib=None) -> np.ndarray:
-    """out [T, h] uint16 bf16 bits."""
+def combine(y_bits: np.ndarray, lay: dict, topk_weights: np.ndarray, lib=None,
+            out: Optional[np.ndarray] = None) -> np.ndarray:
+    """out [T, h] uint16 bf16 bits. With `out` (C-contiguous uint16 [T, h] for
+    the T rows of topk_weights) the result is written there: topk_weights and
+    lay["slot"] may then be a slice of the tokens, y stays whole."""
     lib = lib or load()
     y = np.ascontiguousarray(y_bits, dtype=np.uint16)
     w = np.ascontiguousarray(topk_weights, dtype=np.float32)
     T, k = w.shape
     hidden = y.shape[1]
-    out = np.zeros((T, hidden), np.uint16)
+    if out is None:
+        out = np.zeros((T, hidden), np.uint16)
+    assert out.shape == (T, hidden) and out.dtype == np.uint16
     rc = lib.oracle_combine(T, k, hidden, _p(lay["slot"]), _p(w), _p(y), _p(out))
     if rc != 0:
         raise OracleError(rc, "oracle_combine")

@@ -53,6 +53,21 @@ def test_group_bytes_one_group_and_conservation():
     assert rest == crossings * 2 * h * 4
 
 
+@pytest.mark.parametrize("relay,fp8", [(False, False), (True, True)])
+def test_threaded_cpu_layer_equals_single_threaded(relay, fp8):
+    """The threaded baseline runs the unchanged oracle on token slices; the
+    layer's output is the same bytes as the single-threaded run."""
+    from concurrent.futures import ThreadPoolExecutor
+    from combine_epx_get_amd import workloads as W
+    w = W.WORKLOADS["tiny"]
+    d = W.make_inputs(w)
+    y = W.random_bf16((w.num_tokens * w.topk, w.hidden), seed=3)
+    one = bench.cpu_layer(w, d, y, relay, fp8)
+    with ThreadPoolExecutor(max_workers=5) as pool:
+        many = bench.cpu_layer(w, d, y, relay, fp8, pool, 5)
+    assert np.array_equal(one, many)
+
+
 @pytest.mark.gpu
 def test_bench_prints_one_json_line():
     import torch
@@ -75,11 +90,16 @@ def test_bench_prints_one_json_line():
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     assert 0 < r["copy_ceiling_GBs"] < 2 * r["peak"]
-    assert d["cache"].startswith("warm") and d["event_every"] == 3   # at most the step count
+    assert d["cache"].startswith("warm") and d["event_every"] == 1
+    assert r["timing"].startswith("HIP events bound")
     for v in d["kernels"].values():
         assert v["us_min"] <= v["us_median"] <= v["us_max"] and v["us_min"] <= v["us"] <= v["us_max"]
+    # the cold-cache figures of the same kernels ride along
+    assert d["cold"]["cache"].startswith("cold") and set(d["cold"]["kernels"]) == set(d["kernels"])
+    assert all(v["us"] > 0 for v in d["cold"]["kernels"].values())
     c = d["cpu_baseline"]
-    assert c["kind"] == "oracle" and c["cores"] == 1 and c["value"] > 0
+    assert c["kind"] == "oracle" and c["cores"] == bench.cpu_threads() and c["value"] > 0
+    assert c["single_thread"]["value"] > 0 and c["cpu_model"]
 
 
 @pytest.mark.gpu
@@ -95,7 +115,7 @@ def test_bench_cold_cache_and_fused_lines():
         assert rc == 0
         d = json.loads(buf.getvalue().strip().splitlines()[-1])
         if "--cold" in extra:
-            assert d["cache"].startswith("cold")
+            assert d["cache"].startswith("cold") and d["warm"]["cache"].startswith("warm")
             # under --cold the step time is the layer's event time
             assert abs(d["ms_per_step"] * 1e3 - d["us_per_layer"]) < 0.02 * d["us_per_layer"] + 0.01
         else:
