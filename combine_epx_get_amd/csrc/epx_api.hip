@@ -3,7 +3,16 @@
 // fails a check launches nothing.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "epx_internal.h"
+
+// Scratch of epx_layout_dispatch_noalloc: the layout workspace for callers
+// that cannot allocate. One copy per GPU (each device holds its own at its
+// own address), kept until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: host code only ever uses the
+// device address that hipGetSymbolAddress returns for it.
+static __device__ __align__(256) int32_t scratch[EPX_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
 
 namespace epx {
 TimingHook &timing_hook()
@@ -118,6 +127,28 @@ epx_status check_layout(const Geometry &g, const epx_layout *L)
 
 epx_status from_hip(hipError_t e) { return e == hipSuccess ? EPX_OK : EPX_ERR_DEVICE; }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+int32_t *g_scratch_ptr[kMaxDevices];
+
+epx_status scratch_on_current_device(int32_t **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return EPX_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+            return EPX_ERR_DEVICE;
+        g_scratch_ptr[dev] = (int32_t *)ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return EPX_OK;
+}
+
 // The dispatch arguments (T > 0 for the pointers).
 epx_status check_dispatch(const Geometry &g, const void *x, int32_t hidden, int32_t out_dtype,
                           const void *recv, const float *recv_scales, int64_t capacity_rows)
@@ -161,6 +192,31 @@ epx_status dispatch_impl(const epx_problem *p, const epx_layout *layout, int gro
     if (out_dtype == EPX_BF16)
         return from_hip(epx::launch_dispatch_bf16(g, *layout, x, hidden, recv, group, s));
     return from_hip(epx::launch_dispatch_fp8(g, *layout, x, hidden, recv, recv_scales, group, s));
+}
+
+// epx_layout_dispatch after the problem and layout checks; `L` carries the
+// workspace to use.
+epx_status layout_dispatch_checked(const Geometry &g, const int32_t *topk_idx, const epx_layout &L,
+                                   const void *x, int32_t hidden, int32_t out_dtype, void *recv,
+                                   float *recv_scales, int64_t capacity_rows, void *stream)
+{
+    if (g.T > 0 && (!topk_idx || !aligned(topk_idx, 4)))
+        return EPX_ERR_ARG;
+    epx_status st = check_dispatch(g, x, hidden, out_dtype, recv, recv_scales, capacity_rows);
+    if (st != EPX_OK)
+        return st;
+    const hipStream_t s = (hipStream_t)stream;
+    const bool fp8 = out_dtype == EPX_FP8_E4M3;
+    hipError_t err = hipSuccess;
+    if (g.T > 0 && epx::launch_layout_dispatch(g, topk_idx, L, x, hidden, fp8, recv, recv_scales, s, &err))
+        return from_hip(err);
+    if (epx::launch_layout_assign_dispatch(g, topk_idx, L, x, hidden, fp8, recv, recv_scales, s, &err))
+        return from_hip(err);
+    if ((st = from_hip(epx::launch_layout(g, topk_idx, L, s))) != EPX_OK || g.T == 0)
+        return st;
+    if (!fp8)
+        return from_hip(epx::launch_dispatch_bf16(g, L, x, hidden, recv, -1, s));
+    return from_hip(epx::launch_dispatch_fp8(g, L, x, hidden, recv, recv_scales, -1, s));
 }
 
 epx_status combine_impl(const epx_problem *p, const epx_layout *layout, int group, const void *y,
@@ -220,6 +276,8 @@ const char *epx_status_string(epx_status s)
         return "output buffer smaller than required";
     case EPX_ERR_DEVICE:
         return "HIP launch or runtime failure";
+    case EPX_ERR_SCRATCH:
+        return "problem too large for the library's static scratch (epx_layout_dispatch_noalloc)";
     }
     return "unknown status";
 }
@@ -273,25 +331,36 @@ epx_status epx_layout_dispatch(const epx_problem *p, const int32_t *topk_idx,
         return st;
     if ((st = check_layout(g, layout)) != EPX_OK)
         return st;
-    if (g.T > 0 && (!topk_idx || !aligned(topk_idx, 4)))
-        return EPX_ERR_ARG;
-    if ((st = check_dispatch(g, x, hidden, out_dtype, recv, recv_scales, capacity_rows)) != EPX_OK)
-        return st;
-    const hipStream_t s = (hipStream_t)stream;
-    const bool fp8 = out_dtype == EPX_FP8_E4M3;
-    hipError_t err = hipSuccess;
-    if (g.T > 0 &&
-        epx::launch_layout_dispatch(g, topk_idx, *layout, x, hidden, fp8, recv, recv_scales, s, &err))
-        return from_hip(err);
-    if (epx::launch_layout_assign_dispatch(g, topk_idx, *layout, x, hidden, fp8, recv, recv_scales,
-                                           s, &err))
-        return from_hip(err);
-    if ((st = from_hip(epx::launch_layout(g, topk_idx, *layout, s))) != EPX_OK || g.T == 0)
-        return st;
-    if (!fp8)
-        return from_hip(epx::launch_dispatch_bf16(g, *layout, x, hidden, recv, -1, s));
-    return from_hip(epx::launch_dispatch_fp8(g, *layout, x, hidden, recv, recv_scales, -1, s));
+    return layout_dispatch_checked(g, topk_idx, *layout, x, hidden, out_dtype, recv, recv_scales,
+                                   capacity_rows, stream);
 }
+
+epx_status epx_layout_dispatch_noalloc(const epx_problem *p, const int32_t *topk_idx,
+                                       const epx_layout *layout, const void *x, int32_t hidden,
+                                       int32_t out_dtype, void *recv, float *recv_scales,
+                                       int64_t capacity_rows, void *stream)
+{
+    HookScope hook_scope;
+    Geometry g;
+    epx_status st = make_geometry(p, &g);
+    if (st != EPX_OK)
+        return st;
+    if (!layout)
+        return EPX_ERR_ARG;
+    int64_t sizes[EPX_LAYOUT_NARRAYS];
+    sizes_of(g, sizes);
+    if (sizes[EPX_L_WORKSPACE] * (int64_t)sizeof(int32_t) > (int64_t)EPX_NOALLOC_SCRATCH_BYTES)
+        return EPX_ERR_SCRATCH;   // checked before any HIP call
+    epx_layout L = *layout;
+    L.workspace = nullptr;
+    if ((st = scratch_on_current_device(&L.workspace)) != EPX_OK)
+        return st;
+    if ((st = check_layout(g, &L)) != EPX_OK)
+        return st;
+    return layout_dispatch_checked(g, topk_idx, L, x, hidden, out_dtype, recv, recv_scales,
+                                   capacity_rows, stream);
+}
+
 
 epx_status epx_dispatch_group(const epx_problem *p, const epx_layout *layout, int32_t group,
                               const void *x, int32_t hidden, int32_t out_dtype, void *recv,

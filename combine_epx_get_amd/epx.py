@@ -27,7 +27,8 @@ BF16 = 0
 FP8_E4M3 = 1
 F32 = 2
 
-STATUS = {0: "EPX_OK", 1: "EPX_ERR_ARG", 2: "EPX_ERR_INDEX", 3: "EPX_ERR_CAPACITY", 4: "EPX_ERR_DEVICE"}
+STATUS = {0: "EPX_OK", 1: "EPX_ERR_ARG", 2: "EPX_ERR_INDEX", 3: "EPX_ERR_CAPACITY", 4: "EPX_ERR_DEVICE",
+          5: "EPX_ERR_SCRATCH"}
 
 LAYOUT_FIELDS = ["expert_count", "expert_offset", "rank_rows", "rank_tokens", "rank_offset",
                  "host_tokens", "host_offset", "slot", "row_token", "relay_slot", "relay_token",
@@ -64,6 +65,8 @@ _lib.epx_combine_relay_finish.argtypes = [ctypes.POINTER(epx_problem), ctypes.PO
                                           ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P]
 _lib.epx_layout_dispatch.argtypes = [ctypes.POINTER(epx_problem), _P, ctypes.POINTER(epx_layout), _P,
                                      ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int64, _P]
+_lib.epx_layout_dispatch_noalloc.argtypes = [ctypes.POINTER(epx_problem), _P, ctypes.POINTER(epx_layout), _P,
+                                             ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int64, _P]
 _lib.epx_dispatch_group.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_layout), ctypes.c_int32,
                                     _P, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int64, _P]
 _lib.epx_combine_group.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(epx_layout), ctypes.c_int32,
@@ -76,7 +79,7 @@ _lib.epx_status_string.restype = ctypes.c_char_p
 for _f in ("epx_layout_sizes", "epx_get_layout", "epx_dispatch", "epx_combine", "epx_read_error",
            "epx_f32_to_e4m3", "epx_relay_fanout", "epx_combine_relay_partials",
            "epx_combine_relay_finish", "epx_plan_swaps", "epx_dispatch_group", "epx_combine_group",
-           "epx_layout_dispatch", "epx_time_next_call"):
+           "epx_layout_dispatch", "epx_time_next_call", "epx_layout_dispatch_noalloc"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.epx_abi_version.restype = ctypes.c_int32
 NARRAYS = len(LAYOUT_FIELDS)
@@ -201,6 +204,23 @@ def epx_layout_dispatch(problem: epx_problem, topk_idx: torch.Tensor, layout: La
                                     x.data_ptr(), hidden, out_dtype, recv.data_ptr(), scales_ptr,
                                     recv.shape[0], _stream(stream)),
            "epx_layout_dispatch")
+
+
+def epx_layout_dispatch_noalloc(problem: epx_problem, topk_idx: torch.Tensor, layout, x: torch.Tensor,
+                                out_dtype: int, recv: torch.Tensor, recv_scales: Optional[torch.Tensor] = None,
+                                stream=None) -> None:
+    """epx_layout_dispatch with the library's static scratch in place of the
+    layout's workspace. `layout` is a Layout or an epx_layout struct (its
+    workspace may be NULL)."""
+    _need(topk_idx, torch.int32, "topk_idx", 2)
+    if tuple(topk_idx.shape) != (problem.num_tokens, problem.topk):
+        raise ValueError(f"topk_idx shape {tuple(topk_idx.shape)} != (T, k)")
+    hidden, scales_ptr = _dispatch_args(problem, x, out_dtype, recv, recv_scales)
+    struct = layout.struct if isinstance(layout, Layout) else layout
+    _check(_lib.epx_layout_dispatch_noalloc(ctypes.byref(problem), topk_idx.data_ptr(), ctypes.byref(struct),
+                                            x.data_ptr(), hidden, out_dtype, recv.data_ptr(), scales_ptr,
+                                            recv.shape[0], _stream(stream)),
+           "epx_layout_dispatch_noalloc")
 
 
 def epx_dispatch_group(problem: epx_problem, layout: Layout, group: int, x: torch.Tensor, out_dtype: int,

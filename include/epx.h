@@ -20,7 +20,9 @@
  *
  * Conventions for every call:
  *  - Every array argument is a DEVICE pointer the caller allocated; the
- *    library allocates nothing, frees nothing and keeps no global state.
+ *    library allocates nothing and frees nothing. Its only state is the
+ *    static scratch array of epx_layout_dispatch_noalloc (one per GPU) and
+ *    the per-thread measurement hook of epx_time_next_call.
  *    Activation pointers (x, recv, y, out) must be 16-byte aligned.
  *  - Calls are asynchronous and ordered on the HIP stream passed as `stream`
  *    (a hipStream_t; NULL = the null stream). No call synchronises the host,
@@ -45,7 +47,7 @@
 extern "C" {
 #endif
 
-#define EPX_ABI_VERSION 3
+#define EPX_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define EPX_API __attribute__((visibility("default")))
@@ -58,8 +60,13 @@ typedef enum {
     EPX_ERR_ARG = 1,      /* bad pointer, alignment, geometry or size     */
     EPX_ERR_INDEX = 2,    /* an expert id out of range (device-detected)  */
     EPX_ERR_CAPACITY = 3, /* an output buffer smaller than required       */
-    EPX_ERR_DEVICE = 4    /* a HIP launch or runtime call failed          */
+    EPX_ERR_DEVICE = 4,   /* a HIP launch or runtime call failed          */
+    EPX_ERR_SCRATCH = 5   /* problem too large for the static scratch of
+                             epx_layout_dispatch_noalloc                  */
 } epx_status;
+
+/* Size of the static scratch array behind epx_layout_dispatch_noalloc. */
+#define EPX_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /* Transport layout of dispatch (digest section 3.2, Figure 3).
  * PER_EXPERT: one copy of a token per destination expert (DeepEP's Mode 1).
@@ -225,6 +232,31 @@ EPX_API epx_status epx_layout_dispatch(const epx_problem *p, const int32_t *topk
                                        const epx_layout *layout, const void *x, int32_t hidden,
                                        int32_t out_dtype, void *recv, float *recv_scales,
                                        int64_t capacity_rows, void *stream);
+
+/* epx_layout_dispatch for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The same arguments and the same results, bit for bit, except
+ * that layout->workspace is not used (it may be NULL): the layout kernels'
+ * scratch is instead a static device array inside the library,
+ * EPX_NOALLOC_SCRATCH_BYTES (16 MiB) on every GPU the library runs on, held
+ * until the process ends. Its device address is looked up on the first call
+ * on each device (with that device current). Nothing in it has to start at
+ * any value: every call overwrites what it reads.
+ * Limit: the problem's workspace (epx_layout_sizes, EPX_L_WORKSPACE, int32
+ * elements) must fit in the array, else EPX_ERR_SCRATCH before anything is
+ * launched or any HIP call is made. At E = 256, top-8 that holds batches of
+ * well over 100 000 tokens; decode batches (the single-launch sizes) do not
+ * use it at all.
+ * All calls on one GPU share its array, and it keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other host
+ * threads, graphs replayed concurrently) race and give undefined results.
+ * Calls ordered on one stream are safe. No hipMalloc, hipFree or other
+ * allocating routine is called. */
+EPX_API epx_status epx_layout_dispatch_noalloc(const epx_problem *p, const int32_t *topk_idx,
+                                               const epx_layout *layout, const void *x,
+                                               int32_t hidden, int32_t out_dtype, void *recv,
+                                               float *recv_scales, int64_t capacity_rows,
+                                               void *stream);
 
 /* ---- Expert groups (per-expert overlap, digest section 3.3, Figure 4).
  * The problem has num_groups = m > 1; call with group = 0 .. m-1.

@@ -44,8 +44,8 @@ def test_library_exports_every_declared_symbol(epx):
 
 
 def test_abi_version_and_status_strings(epx):
-    assert epx.abi_version() == 3
-    for code in range(5):
+    assert epx.abi_version() == 4
+    for code in range(6):
         assert epx._lib.epx_status_string(code)
 
 
@@ -221,6 +221,27 @@ def test_fused_entry_host_checks(epx):
     # geometry
     bad = epx.make_problem(64, 2, 16, 3, 1, 0, epx.MODE_PER_EXPERT)   # E % R != 0
     assert lib.epx_layout_dispatch(by(bad), A, by(L), A, 256, 0, A, None, 128, None) == 1
+
+
+def test_noalloc_entry_host_checks(epx):
+    """epx_layout_dispatch_noalloc refuses a problem whose workspace would not
+    fit its static scratch before any HIP call (so on any host), and bad
+    problems or a missing layout as epx_layout_dispatch does."""
+    lib = epx._lib
+    by = ctypes.byref
+    A = 0x200000
+    L = _fake_layout(epx, relay=False)
+    big = epx.make_problem(1 << 20, 8, 2048, 64, 2, 0, epx.MODE_PER_EXPERT)
+    ws = epx.epx_layout_sizes(big)[epx.LAYOUT_FIELDS.index("workspace")]
+    assert ws * 4 > (16 << 20)
+    assert lib.epx_layout_dispatch_noalloc(by(big), A, by(L), A, 256, 0, A, None, (1 << 20) * 8, None) == 5
+    p = epx.make_problem(64, 2, 16, 4, 2, 0, epx.MODE_PER_EXPERT)
+    assert lib.epx_layout_dispatch_noalloc(by(p), A, None, A, 256, 0, A, None, 128, None) == 1
+    bad = epx.make_problem(64, 2, 16, 3, 1, 0, epx.MODE_PER_EXPERT)   # E % R != 0
+    assert lib.epx_layout_dispatch_noalloc(by(bad), A, by(L), A, 256, 0, A, None, 128, None) == 1
+    # the large-batch workload fits with room to spare
+    lb = epx.make_problem(4096, 8, 256, 16, 2, 0, epx.MODE_PER_EXPERT)
+    assert epx.epx_layout_sizes(lb)[epx.LAYOUT_FIELDS.index("workspace")] * 4 < (1 << 20)
 
 
 def test_binding_rejects_wrong_tensors(epx):
