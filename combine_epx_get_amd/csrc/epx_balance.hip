@@ -1,13 +1,13 @@
 // epx_balance.hip -- per-step intra-host expert swap planner on gfx950.
 //
-// The digest "Balancing and Beyond: Communication-Centric Optimizations in
-// Expert Parallelism" (section 3.1, Figure 2(b)) fixes the drift of routing
-// between periodic rebalances by swapping experts inside each host every
-// step: the load of a GPU is the sum of its experts' token counts; in each
-// host the heaviest GPU pairs with the lightest, the second heaviest with
-// the second lightest, and so on; each pair takes the single expert swap that
-// most lowers its maximum, and only when the maximum falls by at least tau
-// tokens (tau = t_swap / t_tok: moving the expert's weights must pay off).
+// Per-step expert swaps inside a host ("Balancing and Beyond:
+// Communication-Centric Optimizations in Expert Parallelism", digest section
+// 3.1, Figure 2(b)). Load of rank r = sum of the token counts of the experts
+// in its slots. Per host: sort the ranks by load, descending; rank i of that
+// order is paired with rank n-1-i; for each pair, find the one exchange of
+// an expert of the heavier rank with an expert of the lighter that gives the
+// smallest new pair maximum, and apply it if the maximum drops by at least
+// tau tokens (tau: the weight-move time expressed in per-token time).
 //
 // One workgroup per host. All E counts and the host's slots (rank-major, epr
 // per rank) are staged in LDS with independent loads; rank loads are summed

@@ -153,13 +153,18 @@ __device__ __forceinline__ uint32_t e4m3_pair(float a, float b)
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false) & 0xFFFFu;
 }
 
-// x / s, correctly rounded, for a block scale s >= 2^-100 and |x| <= 448 s:
-// the refinement of the IEEE division expansion (reciprocal y refined once
-// per scale, two fma corrections per quotient) without its range scaling,
-// which these operands never need; the sign is restored for zero x. Over
-// every bf16 pair (x, amax) with |x| <= amax and s = amax / 448 >= 2^-100 it
-// gives the same E4M3 code as the IEEE quotient (its last bit can differ only
-// for quotients far below the smallest code).
+// x / s for a block scale s >= 2^-100 and |x| <= 448 s, by fma-based
+// division (P. Markstein, "Computation of elementary functions on the IBM
+// RISC System/6000 processor", IBM J. Res. Dev. 34(1), 1990): the hardware
+// reciprocal seed of s is refined by one Newton-Raphson step once per block
+// (refined_reciprocal), then each quotient q0 = x*y takes two residual
+// corrections r = fma(-s, q, x), q' = fma(r, y, q). The range scaling that a
+// general division needs is left out, since these operands never need it;
+// the sign is restored for zero x. Over every bf16 pair (x, amax) with
+// |x| <= amax and s = amax / 448 >= 2^-100 it gives the same E4M3 code as the
+// correctly rounded quotient (its last bit can differ only for quotients far
+// below the smallest code); tests/test_fp8_quotient_gpu.py checks every such
+// pair, and the smaller scales, through the dispatch.
 __device__ __forceinline__ float div_by_scale(float x, float s, float y)
 {
     const float q0 = x * y;

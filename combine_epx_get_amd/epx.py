@@ -308,6 +308,12 @@ def epx_relay_fanout(problem: epx_problem, layout: Layout, relay_rows: torch.Ten
     if fp8:
         _need(relay_scales, torch.float32, "relay_scales", 2)
         _need(recv_scales, torch.float32, "recv_scales", 2)
+        # the kernel reads relay_scales[r] for relay rows r and writes
+        # recv_scales[o] for per-expert rows o: one scale per 128 channels
+        if tuple(relay_scales.shape) != (relay_rows.shape[0], hidden // 128):
+            raise ValueError("relay_scales: need [relay_rows, hidden/128]")
+        if tuple(recv_scales.shape) != (recv.shape[0], hidden // 128):
+            raise ValueError("recv_scales: need [capacity_rows, hidden/128]")
     _check(_lib.epx_relay_fanout(ctypes.byref(problem), ctypes.byref(layout.struct), relay_rows.data_ptr(),
                                  relay_scales.data_ptr() if fp8 else None, relay_rows.shape[0], hidden,
                                  FP8_E4M3 if fp8 else BF16, recv.data_ptr(),

@@ -570,10 +570,9 @@ int oracle_relay_finish(int32_t T, int32_t H, int32_t hidden, int32_t bf16_in,
 /* Expert groups (per-expert overlap)                                  */
 /* ------------------------------------------------------------------ */
 /*
- * Digest section 3.3 and Figure 4: instead of splitting the batch, the
- * experts are split into m groups (2 or 4) that are dispatched, computed and
- * combined one after another, the whole batch in every group, so each expert
- * weight is loaded once. Every GPU must have work in every group for the
+ * Digest section 3.3 and Figure 4: the split is over experts, not over the
+ * batch: m groups (2 or 4) in turn, each over the whole batch, so every
+ * expert's weights are read once. Every GPU must have work in every group for the
  * overlap to exist, so group g holds, on every rank, the local experts i
  * (i = e mod epr) with i / (epr / m) == g.
  *
@@ -700,11 +699,11 @@ int oracle_combine_grouped(int32_t T, int32_t k, int32_t E, int32_t R, int32_t m
 /* Per-step intra-host expert swap planner                             */
 /* ------------------------------------------------------------------ */
 /*
- * Digest section 3.1 and Figure 2(b): every step the load of each GPU is the
- * sum of its experts' token counts; inside each host the heaviest GPU pairs
- * with the lightest, the second heaviest with the second lightest, and so
- * on; each pair takes the one expert swap that most lowers its maximum, and
- * only when the maximum falls by at least tau tokens.
+ * Digest section 3.1 and Figure 2(b). Load of rank r = sum over its slots of
+ * the experts' token counts. Per host: ranks sorted by load, descending;
+ * the i-th of that order is paired with the (n-1-i)-th; each pair gets the
+ * single expert exchange with the smallest new pair maximum, applied when
+ * the maximum drops by at least tau tokens.
  *
  * Placement: slot_expert[r * epr + i] is the expert in slot i of rank r.
  * Ties: ranks are ordered by load descending, then rank index ascending;

@@ -43,11 +43,14 @@ def test_oracle_never_refers_to_the_package():
 
 def test_only_the_baseline_and_smoke_call_the_oracle():
     bench = open(os.path.join(ROOT, "bench.py"), encoding="utf-8").read()
-    # the oracle is imported inside the CPU-baseline function only
+    # the oracle is imported inside the CPU-baseline leg only (one layer of
+    # the oracle, and its timing)
     uses = [m.start() for m in re.finditer(r"import oracle|from oracle", bench)]
-    start = bench.index("def cpu_baseline(")
-    end = bench.index("\ndef ", start + 1)
-    assert uses and all(start < u < end for u in uses)
+    spans = []
+    for fn in ("def cpu_layer(", "def cpu_baseline("):
+        start = bench.index(fn)
+        spans.append((start, bench.index("\ndef ", start + 1)))
+    assert uses and all(any(a < u < b for a, b in spans) for u in uses)
     entry = open(os.path.join(ROOT, "__graft_entry__.py"), encoding="utf-8").read()
     uses = [m.start() for m in re.finditer(r"import oracle|from oracle", entry)]
     smoke, build = entry.index("def smoke("), entry.index("def build(")

@@ -145,3 +145,26 @@ def test_relay_calls_need_relay_mode(epx):
     with pytest.raises(epx.EpxError) as ei:
         epx.epx_relay_fanout(p, L, rows, rows)
     assert ei.value.code == 1
+
+
+def test_fanout_binding_checks_scale_shapes(epx):
+    """Undersized fp8 scale tensors are refused by the binding before the
+    call (the kernel would read and write one scale per 128 channels of every
+    relay and per-expert row)."""
+    T, k, E, R, H, h = 64, 2, 16, 4, 2, 256
+    p = epx.make_problem(T, k, E, R, H, 0, epx.MODE_HOST_RELAY)
+    L = epx.Layout(p)
+    epx.epx_get_layout(p, _dev(np.tile(np.array([[1, 9]], np.int32), (T, 1))), L)
+    cap = epx.relay_capacity(p)
+    rows = torch.zeros((cap, h), dtype=torch.uint8, device="cuda")
+    recv = torch.zeros((T * k, h), dtype=torch.uint8, device="cuda")
+    good_rs = torch.zeros((cap, h // 128), dtype=torch.float32, device="cuda")
+    good_sc = torch.zeros((T * k, h // 128), dtype=torch.float32, device="cuda")
+    short_rs = torch.zeros((cap - 1, h // 128), dtype=torch.float32, device="cuda")
+    short_sc = torch.zeros((T * k, h // 128 - 1), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        epx.epx_relay_fanout(p, L, rows, recv, short_rs, good_sc)
+    with pytest.raises(ValueError):
+        epx.epx_relay_fanout(p, L, rows, recv, good_rs, short_sc)
+    epx.epx_relay_fanout(p, L, rows, recv, good_rs, good_sc)
+    torch.cuda.synchronize()
