@@ -68,7 +68,8 @@ class Workload:
 # decode variant gives imbalance ratios inside the digest's measured range.
 # The rank_* shapes are the source ranks of the DeepEP rank-imbalance issue
 # (2 machines x 8 ranks): 384 tokens per rank on machine 1 and 64 on machine
-# 2, against 224 everywhere when balanced.
+# 2, against 224 everywhere when balanced. hybridep_bf16 is the HybridEP
+# issue's benchmark shape with per-rank de-duplication.
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload("tiny", 64, 256, 16, 2, 4, 2, "uniform",
                      modes=("per_expert", "relay"), dtypes=("bf16", "fp8"), seed=1),
@@ -88,6 +89,11 @@ WORKLOADS: Dict[str, Workload] = {
                            modes=("per_expert", "relay"), seed=7, my_rank=11),
     "rank_balanced": Workload("rank_balanced", 224, 7168, 256, 8, 16, 2, "uniform",
                               modes=("per_expert", "relay"), seed=8, my_rank=11),
+    # the HybridEP benchmark's shape (4096 tokens per rank, hidden 7168,
+    # top-8, 8 local experts on each of 16 ranks) with one copy per
+    # destination rank: relay mode with every rank its own host
+    "hybridep_bf16": Workload("hybridep_bf16", 4096, 7168, 128, 8, 16, 16, "uniform",
+                              modes=("relay",), seed=9),
 }
 
 

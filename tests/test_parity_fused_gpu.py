@@ -108,7 +108,8 @@ DECODE = [("decode_uniform", "per_expert"), ("decode_skewed", "per_expert"),
           ("tiny", "relay"), ("rank_light", "per_expert"), ("rank_light", "relay"),
           ("rank_heavy", "per_expert"), ("rank_balanced", "relay"),
           # past the decode limits: count, scan and the assign-and-copy launch
-          ("large_batch", "per_expert"), ("large_batch", "relay"), ("fp8_dispatch", "relay")]
+          ("large_batch", "per_expert"), ("large_batch", "relay"), ("fp8_dispatch", "relay"),
+          ("hybridep_bf16", "relay")]
 
 
 @pytest.mark.parametrize("name,mode", DECODE)

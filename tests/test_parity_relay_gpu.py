@@ -78,7 +78,8 @@ def run_relay_case(epx, x_bits, idx, w, E, R, H, s, what=""):
     return ora
 
 
-RELAY_WORKLOADS = ["tiny", "decode_skewed", "decode_skewed_s06", "fp8_dispatch", "large_batch"]
+RELAY_WORKLOADS = ["tiny", "decode_skewed", "decode_skewed_s06", "fp8_dispatch", "large_batch",
+                   "hybridep_bf16"]
 
 
 @pytest.mark.parametrize("name", RELAY_WORKLOADS)
