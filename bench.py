@@ -152,6 +152,97 @@ def load_counter_traffic(kernel: str, tag: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def workload_tag(args) -> str:
+    """workload_mode_payload[_gM][_fused]: the name of a configuration's
+    committed profile summaries."""
+    from combine_epx_get_amd import workloads as W0
+    w0 = W0.WORKLOADS[args.workload]
+    mode = args.mode or ("relay" if args.relay_receive else w0.modes[0])
+    tag = f"{args.workload}_{mode}_{args.dtype or w0.dtypes[0]}"
+    if args.groups > 1:
+        tag += f"_g{args.groups}"
+    if args.relay_receive:
+        tag += "_receive" + ("_bf16partials" if args.partials == "bf16" else "")
+    if args.swap_planner is not None:
+        tag += f"_swap{args.swap_planner}"
+    if args.fused:
+        tag += "_fused"
+    return tag
+
+
+def short_kernel_name(name: str) -> str:
+    """A demangled kernel name without namespaces, template arguments or
+    parameters (combine_kernel<2>(...) -> combine_kernel)."""
+    n = name[5:] if name.startswith("void ") else name
+    n = n.replace("epx::(anonymous namespace)::", "")
+    depth = 0
+    for i, ch in enumerate(n):
+        if ch == "<":
+            if depth == 0 and i > 0:
+                return n[:i]
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return n[:i]
+    return n
+
+
+def ingest_trace(stats_csv: str, tag: str, command: str) -> str:
+    """Write profiles/<tag>.md from a rocprofv3 --kernel-trace --stats run:
+    the per-kernel call counts and durations, stamped with the hash of the
+    kernel sources they were taken on, plus the HBM traffic of the same
+    workload's committed counter summaries that are current."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    out = [f"# {tag}: rocprofv3 kernel trace", "",
+           f"sources_hash: {kernel_sources_hash()} (every file of combine_epx_get_amd/csrc; bench.py "
+           f"reports these averages only while the sources hash to it)", "",
+           "Command (on the GPU box; $REPO is the repository root):", "", "    " + command, "",
+           "| kernel | calls | average µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['Percentage']):.1f} |")
+    counters = []
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"counters_*_{tag}.json"))):
+        d = json.load(open(path))
+        if d.get("sources_hash") == kernel_sources_hash(d["kernel"]):
+            counters.append(d)
+    if counters:
+        out += ["", "HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, scaled by a "
+                    "plain copy of known size in the same runs; from profiles/counters_*_" + tag + ".json):",
+                "", "| kernel | read MB | write MB | total MB | fetch factor | write factor |",
+                "|---|---|---|---|---|---|"]
+        for d in counters:
+            cal = d["calibration"]
+            out.append(f"| {d['kernel']} | {d['hbm_read_bytes_per_launch'] / 1e6:.2f} | "
+                       f"{d['hbm_write_bytes_per_launch'] / 1e6:.2f} | {d['hbm_bytes_per_launch'] / 1e6:.2f} | "
+                       f"{cal['fetch_factor']} | {cal['write_factor']} |")
+        out += ["", "Counter commands:", ""] + ["    " + c for c in counters[0]["command"].split("  ;  ")]
+    path = os.path.join(ROOT, "profiles", f"{tag}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    return path
+
+
+def load_trace_average(kernel: str, tag: str):
+    """The committed trace's average µs for `kernel` on this workload, if the
+    trace was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{tag}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    stamp = [l for l in text.splitlines() if l.startswith("sources_hash: ")]
+    if not stamp or stamp[0].split()[1] != kernel_sources_hash():
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.split("|")]
+        if len(cells) > 4 and cells[1] == kernel:
+            return float(cells[3])
+    return None
+
+
 KERNEL_NAMES = ("dispatch_bf16_kernel", "dispatch_fp8_kernel", "combine_kernel",
                 "relay_fanout_kernel", "relay_partials_kernel", "relay_finish_kernel",
                 "layout_small_kernel", "layout_count_kernel", "layout_scan_kernel",
@@ -396,23 +487,27 @@ def main(argv=None) -> int:
                          "(evicts the 256 MB Infinity Cache and L2; the flush is outside every "
                          "timing). Either way the line also carries the other cache state's "
                          "per-kernel times")
+    ap.add_argument("--other-cache", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the other cache state (cold beside a warm headline, warm beside "
+                         "a cold one); profiling runs turn it off so that the trace covers the "
+                         "headline's steps only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/counters_*.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--ingest-trace", metavar="KERNEL_STATS_CSV",
+                    help="write profiles/<workload tag>.md from a rocprofv3 --kernel-trace --stats "
+                         "run (its kernel_stats.csv) and exit")
     ap.add_argument("--ingest-command", default="", help="the profiling command, recorded verbatim")
     args = ap.parse_args(argv)
 
-    if args.ingest_counters:
-        w0 = args.workload
-        from combine_epx_get_amd import workloads as W0
-        tag0 = f"{w0}_{args.mode or W0.WORKLOADS[w0].modes[0]}_{args.dtype or W0.WORKLOADS[w0].dtypes[0]}"
-        if args.groups > 1:
-            tag0 += f"_g{args.groups}"
-        if args.fused:
-            tag0 += "_fused"
-        for pth in ingest_counters(*args.ingest_counters, tag0, args.ingest_command):
-            print(pth)
+    if args.ingest_counters or args.ingest_trace:
+        tag0 = workload_tag(args)
+        if args.ingest_trace:
+            print(ingest_trace(args.ingest_trace, tag0, args.ingest_command))
+        else:
+            for pth in ingest_counters(*args.ingest_counters, tag0, args.ingest_command):
+                print(pth)
         return 0
 
     if args.gpus != 1:
@@ -590,7 +685,7 @@ def main(argv=None) -> int:
     wall, recs = timed_steps(args.steps, args.cold)
     # the other cache state, for the same kernels: cold steps (flush before
     # each) beside a warm headline, warm steps beside a cold one
-    _, recs_other = timed_steps(args.steps, not args.cold)
+    recs_other = timed_steps(args.steps, not args.cold)[1] if args.other_cache else None
     del scratch
 
     graph_us = None
@@ -673,7 +768,7 @@ def main(argv=None) -> int:
         return out, np.asarray(layer, dtype=np.float64)
 
     per_kernel, layer_us = kernel_times(recs)
-    other_kernel, other_layer_us = kernel_times(recs_other)
+    other_kernel, other_layer_us = kernel_times(recs_other) if recs_other else (None, None)
     hipev.release()
     # the flush is not part of the layer: cold steps take their time from the
     # kernel events, warm steps from the wall clock
@@ -688,24 +783,30 @@ def main(argv=None) -> int:
              "dispatch_g": "dispatch_fp8_kernel" if fp8 else "dispatch_bf16_kernel",
              "combine_g": "combine_group_kernel",
              "layout_dispatch": fused_kernel(T, k, w.num_experts, relay, fp8)}[dom.rstrip("0123456789")]
-    tag = f"{args.workload}_{mode}_{dtype}" + (f"_g{m}" if m > 1 else "") + ("_fused" if fused else "")
+    tag = workload_tag(args)
     traffic = load_counter_traffic(kname, tag)
+    trace_us = load_trace_average(kname, tag)
     roofline = {"bound": "hbm", "kernel": kname,
                 "achieved": round(per_kernel[dom]["GBs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(per_kernel[dom]["frac_peak"], 4), "traffic": traffic,
                 "algorithmic_bytes": per_kernel[dom]["bytes"],
                 "timing": "HIP events bound to the kernels' dispatch packets (hipExtLaunchKernel)",
+                "profile": ({"file": f"profiles/{tag}.md", "trace_avg_us": trace_us,
+                             "event_avg_us": round(per_kernel[dom]["us"], 3)}
+                            if trace_us is not None else None),
                 "copy_ceiling_GBs": round(copy_ceiling(torch, dev), 1)}
 
     def rounded(pk):
         return {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                 for n, v in pk.items()}
 
-    other = {"cache": "warm (back-to-back steps)" if args.cold else
-             "cold (512 MiB scratch read before each step)",
-             "us_per_layer": round(float(other_layer_us.mean()), 2),
-             "kernels": {n: {"us": round(v["us"], 3), "frac_peak": round(v["frac_peak"], 4)}
-                         for n, v in other_kernel.items()}}
+    other = None
+    if other_kernel is not None:
+        other = {"cache": "warm (back-to-back steps)" if args.cold else
+                 "cold (512 MiB scratch read before each step)",
+                 "us_per_layer": round(float(other_layer_us.mean()), 2),
+                 "kernels": {n: {"us": round(v["us"], 3), "frac_peak": round(v["frac_peak"], 4)}
+                             for n, v in other_kernel.items()}}
 
     cpu = None
     if args.cpu_seconds > 0 and not receive and m == 1:
