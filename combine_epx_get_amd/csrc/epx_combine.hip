@@ -30,15 +30,19 @@ __global__ __launch_bounds__(1024) void combine_kernel(
     __shared__ int32_t s_row[kMaxTopk];
     __shared__ float s_w[kMaxTopk];
     const int64_t t = item_index();
-    if (t >= T || totals[3] != 0)
-        return;   // past the last token, or the layout saw out-of-range expert ids
+    if (t >= T)
+        return;   // past the last token
     const int c_beg = blockIdx.y * slice;
     const int c_end = min(nvec, c_beg + slice);
+    // the error word, the slots and the weights in one round trip
+    const int bad = totals[3];
     if ((int)threadIdx.x < k) {
         s_row[threadIdx.x] = slot[t * k + threadIdx.x];
         s_w[threadIdx.x] = w[t * k + threadIdx.x];
     }
     __syncthreads();
+    if (bad != 0)
+        return;   // the layout saw out-of-range expert ids: the slots are undefined
     for (int c0 = c_beg + threadIdx.x; c0 < c_end; c0 += blockDim.x * CHUNKS) {
         float acc[CHUNKS][8];
 #pragma unroll

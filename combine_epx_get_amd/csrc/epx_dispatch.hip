@@ -57,14 +57,46 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     const int32_t *hi_p, int64_t T)
 {
     const int64_t t = item_index();
-    if (t >= T || totals[3] != 0)
-        return;   // past the last token, or the layout saw out-of-range expert ids
+    if (t >= T)
+        return;   // past the last token
     int lo, hi;
-    row_range(lo_p, hi_p, lo, hi);
     const int c_beg = blockIdx.y * slice;
     const int c_end = min(nvec, c_beg + slice);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const u32x4 *xr = x + t * nvec;
+    if (c_end - c_beg <= kWave * kBurst) {
+        // The slice fits one burst: each wave loads it once, together with
+        // the error word and its destinations (no load waits for another),
+        // and stores the same registers to each of its rows.
+        u32x4 v[kBurst];
+#pragma unroll
+        for (int i = 0; i < kBurst; ++i) {
+            const int c = c_beg + lane + i * kWave;
+            if (c < c_end)
+                v[i] = xr[c];
+        }
+        const int bad = totals[3];
+        int64_t r0 = wave < D ? dest[t * D + wave] : -1;
+        row_range(lo_p, hi_p, lo, hi);
+        if (bad != 0)
+            return;   // the layout saw out-of-range expert ids: its rows are undefined
+        for (int d = wave; d < D; d += kWaves) {
+            const int64_t r = d == wave ? r0 : dest[t * D + d];
+            if (r < lo || r >= hi)
+                continue;
+            u32x4 *dst = recv + r * nvec;
+#pragma unroll
+            for (int i = 0; i < kBurst; ++i) {
+                const int c = c_beg + lane + i * kWave;
+                if (c < c_end)
+                    __builtin_nontemporal_store(v[i], dst + c);
+            }
+        }
+        return;
+    }
+    if (totals[3] != 0)
+        return;   // the layout saw out-of-range expert ids
+    row_range(lo_p, hi_p, lo, hi);
     for (int d = wave; d < D; d += kWaves) {
         const int64_t r = dest[t * D + d];
         if (r < lo || r >= hi)
