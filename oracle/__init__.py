@@ -95,7 +95,7 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.oracle_group_slots.restype = ctypes.c_int
     lib.oracle_combine_grouped.argtypes = [i32] * 6 + [P] * 5
     lib.oracle_combine_grouped.restype = ctypes.c_int
-    lib.oracle_plan_swaps.argtypes = [i32] * 3 + [P] * 2 + [i32] + [P] * 4
+    lib.oracle_plan_swaps.argtypes = [i32] * 3 + [P] * 2 + [i32] + [P] * 5
     lib.oracle_plan_swaps.restype = ctypes.c_int
     for name in ("oracle_f32_to_e4m3_array", "oracle_f32_to_bf16_array", "oracle_e4m3_to_f32_array"):
         getattr(lib, name).argtypes = [P, P, ctypes.c_int64]
@@ -330,7 +330,8 @@ def relay_finish(partials: np.ndarray, lay: dict, num_tokens: int, num_hosts: in
 def plan_swaps(counts: np.ndarray, num_ranks: int, num_hosts: int, tau: int,
                slot_expert: Optional[np.ndarray] = None, lib=None) -> dict:
     """Intra-host swap plan (see oracle_plan_swaps). Returns the placement
-    after the swaps, loads before/after and the per-pair records [.., 7]."""
+    after the swaps, loads before/after, the per-pair records [.., 7] and
+    host_bad [H] (ids outside [0, E) per host; such a host is not planned)."""
     lib = lib or load()
     c = np.ascontiguousarray(counts, dtype=np.int32)
     E, R, H = c.size, num_ranks, num_hosts
@@ -340,11 +341,12 @@ def plan_swaps(counts: np.ndarray, num_ranks: int, num_hosts: int, tau: int,
     la = np.zeros(R, np.int32)
     npair = (R // H) // 2
     sw = np.full((H * max(npair, 0), 7), -1, np.int32)
+    hb = np.zeros(max(H, 1), np.int32)
     rc = lib.oracle_plan_swaps(E, R, H, _p(c), _p(se), tau, _p(out), _p(lb), _p(la),
-                               _p(sw if sw.size else np.zeros(7, np.int32)))
+                               _p(sw if sw.size else np.zeros(7, np.int32)), _p(hb))
     if rc != 0:
         raise OracleError(rc, "oracle_plan_swaps")
-    return {"slot_expert": out, "load_before": lb, "load_after": la, "swaps": sw}
+    return {"slot_expert": out, "load_before": lb, "load_after": la, "swaps": sw, "host_bad": hb[:H]}
 
 
 def f32_to_e4m3(a: np.ndarray, lib=None) -> np.ndarray:

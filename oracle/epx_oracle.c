@@ -718,18 +718,30 @@ int oracle_combine_grouped(int32_t T, int32_t k, int32_t E, int32_t R, int32_t m
  */
 int oracle_plan_swaps(int32_t E, int32_t R, int32_t H, const int32_t *count,
                       const int32_t *slot_expert_in, int32_t tau, int32_t *slot_expert_out,
-                      int32_t *load_before, int32_t *load_after, int32_t *swaps)
+                      int32_t *load_before, int32_t *load_after, int32_t *swaps,
+                      int32_t *host_bad)
 {
     if (E < 1 || R < 1 || H < 1 || E % R != 0 || R % H != 0 || tau < 0)
         return ORC_ERR_ARG;
     const int32_t epr = E / R, rph = R / H, npair = rph / 2;
-    for (int32_t i = 0; i < E; ++i) {
-        if (slot_expert_in[i] < 0 || slot_expert_in[i] >= E)
-            return ORC_ERR_INDEX;
-        slot_expert_out[i] = slot_expert_in[i];
+    /* A host whose slots hold an expert id outside [0, E) is not planned: its
+     * slots are copied, its loads and pair records are -1 (applied 0) and
+     * host_bad[h] is the number of such ids (0 for a planned host). */
+    for (int32_t h = 0; h < H; ++h) {
+        int32_t nbad = 0;
+        for (int32_t i = h * rph * epr; i < (h + 1) * rph * epr; ++i)
+            if (slot_expert_in[i] < 0 || slot_expert_in[i] >= E)
+                nbad += 1;
+        host_bad[h] = nbad;
     }
+    for (int32_t i = 0; i < E; ++i)
+        slot_expert_out[i] = slot_expert_in[i];
     for (int32_t r = 0; r < R; ++r) {
         int64_t load = 0;
+        if (host_bad[r / rph] != 0) {
+            load_before[r] = -1;
+            continue;
+        }
         for (int32_t i = 0; i < epr; ++i)
             load += count[slot_expert_in[r * epr + i]];
         load_before[r] = (int32_t)load;
@@ -749,6 +761,15 @@ int oracle_plan_swaps(int32_t E, int32_t R, int32_t H, const int32_t *count,
                 pos -= 1;
             }
             order[pos] = r;
+        }
+        if (host_bad[h] != 0) {
+            for (int32_t p = 0; p < npair; ++p) {
+                int32_t *rec = swaps + ((int64_t)h * npair + p) * 7;
+                for (int32_t f = 0; f < 6; ++f)
+                    rec[f] = -1;
+                rec[6] = 0;
+            }
+            continue;
         }
         for (int32_t p = 0; p < npair; ++p) {
             int32_t A = order[p], B = order[rph - 1 - p];
@@ -785,6 +806,10 @@ int oracle_plan_swaps(int32_t E, int32_t R, int32_t H, const int32_t *count,
     free(order);
     for (int32_t r = 0; r < R; ++r) {
         int64_t load = 0;
+        if (host_bad[r / rph] != 0) {
+            load_after[r] = -1;
+            continue;
+        }
         for (int32_t i = 0; i < epr; ++i)
             load += count[slot_expert_out[r * epr + i]];
         load_after[r] = (int32_t)load;

@@ -113,6 +113,9 @@ MUTANTS = [
     ("swap ignores the threshold",
      "            int32_t applied = (old_max - best > 0) && (old_max - best >= tau);",
      "            int32_t applied = (old_max - best > 0);"),
+    ("unplanned host reports load 0",
+     "        if (host_bad[r / rph] != 0) {\n            load_before[r] = -1;",
+     "        if (host_bad[r / rph] != 0) {\n            load_before[r] = 0;"),
     ("swap sorts lightest first",
      "                if (load_before[q] > load_before[r] || (load_before[q] == load_before[r] && q < r))",
      "                if (load_before[q] < load_before[r] || (load_before[q] == load_before[r] && q < r))"),
@@ -182,6 +185,7 @@ def _pins():
     for case in TSW.CASES:
         calls.append(lambda c=case: TSW.test_swaps_optimal_and_consistent(c, 5))
     calls.append(TSW.test_degenerate_cases)
+    calls.append(TSW.test_bad_slot_ids_leave_only_their_host_unplanned)
     return calls
 
 

@@ -98,3 +98,31 @@ def test_degenerate_cases():
     counts, se = _random_case(9, 30, 6, 2)
     r = oracle.plan_swaps(counts, 6, 2, 0, se)
     assert r["swaps"].shape == (2, 7)
+
+
+def test_bad_slot_ids_leave_only_their_host_unplanned():
+    """A host whose slots hold an id outside [0, E) is not planned (slots
+    copied, loads and records -1, applied 0, host_bad = the count); every
+    other host's plan equals its plan on a valid placement, since hosts are
+    planned independently (each pair stays inside one host)."""
+    rng = np.random.Generator(np.random.PCG64(17))
+    E, R, H = 64, 8, 4
+    counts = rng.integers(0, 200, size=E).astype(np.int32)
+    se = np.arange(E, dtype=np.int32)
+    bad = se.copy()
+    bad[E // H + 2] = E
+    bad[E // H + 9] = -5
+    got = oracle.plan_swaps(counts, R, H, 0, bad)
+    want = oracle.plan_swaps(counts, R, H, 0, se)
+    assert list(got["host_bad"]) == [0, 2, 0, 0] and not want["host_bad"].any()
+    rph, npair, nslot = R // H, (R // H) // 2, E // H
+    for h in range(H):
+        s_, r_, q_ = (slice(h * nslot, (h + 1) * nslot), slice(h * rph, (h + 1) * rph),
+                      slice(h * npair, (h + 1) * npair))
+        if h == 1:
+            assert np.array_equal(got["slot_expert"][s_], bad[s_])
+            assert np.all(got["load_before"][r_] == -1) and np.all(got["load_after"][r_] == -1)
+            assert np.all(got["swaps"][q_][:, :6] == -1) and np.all(got["swaps"][q_][:, 6] == 0)
+        else:
+            for n, sl in (("slot_expert", s_), ("load_before", r_), ("load_after", r_), ("swaps", q_)):
+                assert np.array_equal(got[n][sl], want[n][sl]), (h, n)
