@@ -480,8 +480,10 @@ def main(argv=None) -> int:
                     help="also time layers captured in a HIP graph (16 per graph) and replayed: the "
                          "layer time without per-launch host overhead (default: on, except with "
                          "--swap-planner)")
-    ap.add_argument("--event-every", type=int, default=1, metavar="N",
-                    help="arm the per-call kernel events on every N-th timed step (1: all)")
+    ap.add_argument("--event-every", type=int, default=4, metavar="N",
+                    help="arm the per-call kernel events on every N-th timed step (1: all); kernels "
+                         "launched with bound events leave larger gaps behind them, so armed steps "
+                         "run slower by the wall clock")
     ap.add_argument("--cold", action="store_true",
                     help="headline from cold steps: a 512 MiB scratch buffer read before every step "
                          "(evicts the 256 MB Infinity Cache and L2; the flush is outside every "

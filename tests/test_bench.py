@@ -90,7 +90,7 @@ def test_bench_prints_one_json_line():
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     assert 0 < r["copy_ceiling_GBs"] < 2 * r["peak"]
-    assert d["cache"].startswith("warm") and d["event_every"] == 1
+    assert d["cache"].startswith("warm") and d["event_every"] == 3   # at most the step count
     assert r["timing"].startswith("HIP events bound")
     for v in d["kernels"].values():
         assert v["us_min"] <= v["us_median"] <= v["us_max"] and v["us_min"] <= v["us"] <= v["us_max"]
