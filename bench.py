@@ -174,7 +174,7 @@ def short_kernel_name(name: str) -> str:
     """A demangled kernel name without namespaces, template arguments or
     parameters (combine_kernel<2>(...) -> combine_kernel)."""
     n = name[5:] if name.startswith("void ") else name
-    n = n.replace("epx::(anonymous namespace)::", "")
+    n = n.replace("(anonymous namespace)::", "").replace("epx::", "")
     depth = 0
     for i, ch in enumerate(n):
         if ch == "<":
