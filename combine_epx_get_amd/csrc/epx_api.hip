@@ -14,6 +14,9 @@
 // device address that hipGetSymbolAddress returns for it.
 static __device__ __align__(256) int32_t scratch[EPX_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
 
+// Bounds-checked builds: accesses that a check skipped, on this device.
+static __device__ unsigned long long violations;
+
 namespace epx {
 TimingHook &timing_hook()
 {
@@ -75,6 +78,8 @@ epx_status make_geometry(const epx_problem *p, Geometry *g)
     g->relay = p->mode == EPX_MODE_HOST_RELAY;
     g->m = m;
     g->epg = g->epr / m;
+    g->viol = nullptr;
+    g->cap = 0;
     return EPX_OK;
 }
 
@@ -133,6 +138,35 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mutex;
 int32_t *g_scratch_ptr[kMaxDevices];
 
+// Device address of `violations` on the current device (checked builds),
+// looked up once per device and kept.
+unsigned long long *g_violations_ptr[kMaxDevices];
+
+epx_status violations_on_current_device(unsigned long long **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return EPX_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_violations_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(violations)) != hipSuccess || ptr == nullptr)
+            return EPX_ERR_DEVICE;
+        g_violations_ptr[dev] = (unsigned long long *)ptr;
+    }
+    *out = g_violations_ptr[dev];
+    return EPX_OK;
+}
+
+// After a call's host checks, before its launches: checked builds point the
+// kernels at the violation counter; release builds do nothing.
+epx_status arm_checks(Geometry &g)
+{
+    if (!epx::kChecked)
+        return EPX_OK;
+    return violations_on_current_device(&g.viol);
+}
+
 epx_status scratch_on_current_device(int32_t **out)
 {
     int dev = -1;
@@ -188,15 +222,19 @@ epx_status dispatch_impl(const epx_problem *p, const epx_layout *layout, int gro
         return st;
     if (g.T == 0)
         return EPX_OK;
+    if ((st = arm_checks(g)) != EPX_OK)
+        return st;
     const hipStream_t s = (hipStream_t)stream;
     if (out_dtype == EPX_BF16)
-        return from_hip(epx::launch_dispatch_bf16(g, *layout, x, hidden, recv, group, s));
-    return from_hip(epx::launch_dispatch_fp8(g, *layout, x, hidden, recv, recv_scales, group, s));
+        return from_hip(
+            epx::launch_dispatch_bf16(g, *layout, x, hidden, recv, capacity_rows, group, s));
+    return from_hip(epx::launch_dispatch_fp8(g, *layout, x, hidden, recv, recv_scales,
+                                             capacity_rows, group, s));
 }
 
 // epx_layout_dispatch after the problem and layout checks; `L` carries the
 // workspace to use.
-epx_status layout_dispatch_checked(const Geometry &g, const int32_t *topk_idx, const epx_layout &L,
+epx_status layout_dispatch_checked(Geometry g, const int32_t *topk_idx, const epx_layout &L,
                                    const void *x, int32_t hidden, int32_t out_dtype, void *recv,
                                    float *recv_scales, int64_t capacity_rows, void *stream)
 {
@@ -205,6 +243,9 @@ epx_status layout_dispatch_checked(const Geometry &g, const int32_t *topk_idx, c
     epx_status st = check_dispatch(g, x, hidden, out_dtype, recv, recv_scales, capacity_rows);
     if (st != EPX_OK)
         return st;
+    if ((st = arm_checks(g)) != EPX_OK)
+        return st;
+    g.cap = capacity_rows;
     const hipStream_t s = (hipStream_t)stream;
     const bool fp8 = out_dtype == EPX_FP8_E4M3;
     hipError_t err = hipSuccess;
@@ -215,8 +256,9 @@ epx_status layout_dispatch_checked(const Geometry &g, const int32_t *topk_idx, c
     if ((st = from_hip(epx::launch_layout(g, topk_idx, L, s))) != EPX_OK || g.T == 0)
         return st;
     if (!fp8)
-        return from_hip(epx::launch_dispatch_bf16(g, L, x, hidden, recv, -1, s));
-    return from_hip(epx::launch_dispatch_fp8(g, L, x, hidden, recv, recv_scales, -1, s));
+        return from_hip(epx::launch_dispatch_bf16(g, L, x, hidden, recv, capacity_rows, -1, s));
+    return from_hip(
+        epx::launch_dispatch_fp8(g, L, x, hidden, recv, recv_scales, capacity_rows, -1, s));
 }
 
 epx_status combine_impl(const epx_problem *p, const epx_layout *layout, int group, const void *y,
@@ -241,12 +283,14 @@ epx_status combine_impl(const epx_problem *p, const epx_layout *layout, int grou
         !aligned(topk_weights, 4))
         return EPX_ERR_ARG;
     const hipStream_t s = (hipStream_t)stream;
-    if (group < 0 || g.m == 1)
-        return from_hip(epx::launch_combine(g, *layout, y, topk_weights, hidden, out, s));
-    if (!carry || !aligned(carry, 16))
+    if (!(group < 0 || g.m == 1) && (!carry || !aligned(carry, 16)))
         return EPX_ERR_ARG;
-    return from_hip(
-        epx::launch_combine_group(g, *layout, group, y, topk_weights, hidden, carry, out, s));
+    if ((st = arm_checks(g)) != EPX_OK)
+        return st;
+    if (group < 0 || g.m == 1)
+        return from_hip(epx::launch_combine(g, *layout, y, y_rows, topk_weights, hidden, out, s));
+    return from_hip(epx::launch_combine_group(g, *layout, group, y, y_rows, topk_weights, hidden,
+                                              carry, out, s));
 }
 
 }  // namespace
@@ -307,6 +351,8 @@ epx_status epx_get_layout(const epx_problem *p, const int32_t *topk_idx, const e
         return st;
     if (g.T > 0 && (!topk_idx || !aligned(topk_idx, 4)))
         return EPX_ERR_ARG;
+    if ((st = arm_checks(g)) != EPX_OK)
+        return st;
     return from_hip(epx::launch_layout(g, topk_idx, *layout, (hipStream_t)stream));
 }
 
@@ -419,9 +465,12 @@ epx_status epx_relay_fanout(const epx_problem *p, const epx_layout *layout,
     if (fp8 && (!relay_scales || !recv_scales || !aligned(relay_scales, 4) || !aligned(recv_scales, 4)))
         return EPX_ERR_ARG;
     const int64_t row_bytes = fp8 ? hidden : (int64_t)hidden * 2;
-    return from_hip(epx::launch_relay_fanout(g, *layout, relay_rows, relay_scales, row_bytes,
+    if ((st = arm_checks(g)) != EPX_OK)
+        return st;
+    return from_hip(epx::launch_relay_fanout(g, *layout, relay_rows, relay_scales,
+                                             relay_capacity_rows, row_bytes,
                                              fp8 ? hidden / epx::kFp8Block : 0, recv, recv_scales,
-                                             (hipStream_t)stream));
+                                             capacity_rows, (hipStream_t)stream));
 }
 
 epx_status epx_combine_relay_partials(const epx_problem *p, const epx_layout *layout,
@@ -447,9 +496,11 @@ epx_status epx_combine_relay_partials(const epx_problem *p, const epx_layout *la
     if (!y || !topk_weights || !partials || !aligned(y, 16) || !aligned(topk_weights, 4) ||
         !aligned(partials, 16))
         return EPX_ERR_ARG;
-    return from_hip(epx::launch_relay_partials(g, *layout, y, topk_weights, hidden,
+    if ((st = arm_checks(g)) != EPX_OK)
+        return st;
+    return from_hip(epx::launch_relay_partials(g, *layout, y, y_rows, topk_weights, hidden,
                                                partial_dtype == EPX_BF16, partials,
-                                               (hipStream_t)stream));
+                                               partial_capacity_rows, (hipStream_t)stream));
 }
 
 epx_status epx_combine_relay_finish(const epx_problem *p, const epx_layout *layout,
@@ -473,8 +524,11 @@ epx_status epx_combine_relay_finish(const epx_problem *p, const epx_layout *layo
         return EPX_OK;
     if (!partials || !out || !aligned(partials, 16) || !aligned(out, 16))
         return EPX_ERR_ARG;
-    return from_hip(epx::launch_relay_finish(g, *layout, partials, partial_dtype == EPX_BF16,
-                                             hidden, out, (hipStream_t)stream));
+    if ((st = arm_checks(g)) != EPX_OK)
+        return st;
+    return from_hip(epx::launch_relay_finish(g, *layout, partials, partial_capacity_rows,
+                                             partial_dtype == EPX_BF16, hidden, out,
+                                             (hipStream_t)stream));
 }
 
 epx_status epx_read_error(const epx_layout *layout, int32_t *bad_count, void *stream)
@@ -516,6 +570,29 @@ epx_status epx_plan_swaps(int32_t num_experts, int32_t num_ranks, int32_t num_ho
     return from_hip(epx::launch_plan_swaps(E, R, H, expert_count, slot_expert_in, tau,
                                            slot_expert_out, rank_load_before, rank_load_after,
                                            swaps, host_bad, (hipStream_t)stream));
+}
+
+epx_status epx_checked_violations(int64_t *count, void *stream)
+{
+    HookScope hook_scope;
+    if (!count)
+        return EPX_ERR_ARG;
+    *count = -1;
+    if (!epx::kChecked)
+        return EPX_ERR_ARG;   // a release build checks nothing
+    unsigned long long *ptr = nullptr;
+    epx_status st = violations_on_current_device(&ptr);
+    if (st != EPX_OK)
+        return st;
+    const hipStream_t s = (hipStream_t)stream;
+    unsigned long long v = 0;
+    const unsigned long long zero = 0;
+    if (hipStreamSynchronize(s) != hipSuccess ||
+        hipMemcpy(&v, ptr, sizeof v, hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(ptr, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess)
+        return EPX_ERR_DEVICE;
+    *count = (int64_t)v;
+    return EPX_OK;
 }
 
 epx_status epx_f32_to_e4m3(const float *in, uint8_t *out, int64_t n, void *stream)

@@ -24,8 +24,8 @@ constexpr int kChunks = 2;   // 16-byte chunks per lane (group combine)
 template <int CHUNKS>
 __global__ __launch_bounds__(1024) void combine_kernel(
     const u32x4 *__restrict__ y, int nvec, int slice, const int32_t *__restrict__ slot,
-    const float *__restrict__ w, int k, u32x4 *__restrict__ out,
-    const int32_t *__restrict__ totals, int64_t T)
+    const float *__restrict__ w, int k, u32x4 *__restrict__ out, int64_t y_rows,
+    unsigned long long *viol, const int32_t *__restrict__ totals, int64_t T)
 {
     __shared__ int32_t s_row[kMaxTopk];
     __shared__ float s_w[kMaxTopk];
@@ -37,7 +37,8 @@ __global__ __launch_bounds__(1024) void combine_kernel(
     // the error word, the slots and the weights in one round trip
     const int bad = totals[3];
     if ((int)threadIdx.x < k) {
-        s_row[threadIdx.x] = slot[t * k + threadIdx.x];
+        const int r = slot[t * k + threadIdx.x];
+        s_row[threadIdx.x] = in_bounds(r, y_rows, viol) ? r : 0;   // checked builds only
         s_w[threadIdx.x] = w[t * k + threadIdx.x];
     }
     __syncthreads();
@@ -103,8 +104,8 @@ __global__ __launch_bounds__(1024) void combine_kernel(
 __global__ __launch_bounds__(1024) void combine_group_kernel(
     const u32x4 *__restrict__ y, int nvec, int slice, const int32_t *__restrict__ slot,
     const float *__restrict__ w, int k, const int32_t *lo_p, const int32_t *hi_p,
-    float4 *__restrict__ carry, u32x4 *__restrict__ out, const int32_t *__restrict__ totals,
-    int64_t T)
+    float4 *__restrict__ carry, u32x4 *__restrict__ out, int64_t y_rows,
+    unsigned long long *viol, const int32_t *__restrict__ totals, int64_t T)
 {
     __shared__ int32_t s_row[kMaxTopk];
     __shared__ float s_w[kMaxTopk];
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(1024) void combine_group_kernel(
         const int j = threadIdx.x;
         const int lo = *lo_p, hi = *hi_p;
         const int r = j < k ? slot[t * k + j] : lo;
-        const bool in = j < k && r >= lo && r < hi;
+        const bool in = j < k && r >= lo && r < hi && in_bounds(r, y_rows, viol);
         const uint64_t bal_in = __ballot(in);
         const uint64_t bal_prior = __ballot(j < k && r < lo);
         const uint64_t bal_later = __ballot(j < k && r >= hi);
@@ -221,8 +222,8 @@ void combine_shape(const Geometry &g, int nvec, int chunks, int &slice, int &thr
 }  // namespace
 
 hipError_t launch_combine_group(const Geometry &g, const epx_layout &L, int group, const void *y,
-                                const float *w, int32_t hidden, float *carry, void *out,
-                                hipStream_t stream)
+                                int64_t y_rows, const float *w, int32_t hidden, float *carry,
+                                void *out, hipStream_t stream)
 {
     const int nvec = hidden / 8;
     int slice, threads;
@@ -232,12 +233,12 @@ hipError_t launch_combine_group(const Geometry &g, const epx_layout &L, int grou
                        nvec, slice, (const int32_t *)L.slot, w, g.k,
                        (const int32_t *)L.group_offset + group * g.R,
                        (const int32_t *)L.group_offset + (group + 1) * g.R, (float4 *)carry,
-                       (u32x4 *)out, (const int32_t *)L.totals, (int64_t)g.T);
+                       (u32x4 *)out, y_rows, g.viol, (const int32_t *)L.totals, (int64_t)g.T);
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const Geometry &g, const epx_layout &L, const void *y, const float *w,
-                          int32_t hidden, void *out, hipStream_t stream)
+hipError_t launch_combine(const Geometry &g, const epx_layout &L, const void *y, int64_t y_rows,
+                          const float *w, int32_t hidden, void *out, hipStream_t stream)
 {
     const int nvec = hidden / 8;
     // Below 256 tokens one 16-byte chunk per lane: twice the workgroups for
@@ -250,12 +251,12 @@ hipError_t launch_combine(const Geometry &g, const epx_layout &L, const void *y,
     const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
     if (chunks == 1)
         launch(combine_kernel<1>, grid, dim3(threads), 0, stream, (const u32x4 *)y,
-                           nvec, slice, (const int32_t *)L.slot, w, g.k, (u32x4 *)out,
-                           (const int32_t *)L.totals, (int64_t)g.T);
+                           nvec, slice, (const int32_t *)L.slot, w, g.k, (u32x4 *)out, y_rows,
+                           g.viol, (const int32_t *)L.totals, (int64_t)g.T);
     else
         launch(combine_kernel<2>, grid, dim3(threads), 0, stream, (const u32x4 *)y,
-                           nvec, slice, (const int32_t *)L.slot, w, g.k, (u32x4 *)out,
-                           (const int32_t *)L.totals, (int64_t)g.T);
+                           nvec, slice, (const int32_t *)L.slot, w, g.k, (u32x4 *)out, y_rows,
+                           g.viol, (const int32_t *)L.totals, (int64_t)g.T);
     return hipGetLastError();
 }
 

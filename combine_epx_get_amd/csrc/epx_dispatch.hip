@@ -53,8 +53,8 @@ __device__ __forceinline__ void row_range(const int32_t *lo_p, const int32_t *hi
 
 __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     const u32x4 *__restrict__ x, int nvec, int slice, const int32_t *__restrict__ dest, int D,
-    u32x4 *__restrict__ recv, const int32_t *__restrict__ totals, const int32_t *lo_p,
-    const int32_t *hi_p, int64_t T)
+    u32x4 *__restrict__ recv, int64_t cap, unsigned long long *viol,
+    const int32_t *__restrict__ totals, const int32_t *lo_p, const int32_t *hi_p, int64_t T)
 {
     const int64_t t = item_index();
     if (t >= T)
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
             return;   // the layout saw out-of-range expert ids: its rows are undefined
         for (int d = wave; d < D; d += kWaves) {
             const int64_t r = d == wave ? r0 : dest[t * D + d];
-            if (r < lo || r >= hi)
+            if (r < lo || r >= hi || !in_bounds(r, cap, viol))
                 continue;
             u32x4 *dst = recv + r * nvec;
 #pragma unroll
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     row_range(lo_p, hi_p, lo, hi);
     for (int d = wave; d < D; d += kWaves) {
         const int64_t r = dest[t * D + d];
-        if (r < lo || r >= hi)
+        if (r < lo || r >= hi || !in_bounds(r, cap, viol))
             continue;
         u32x4 *dst = recv + r * nvec;
         for (int c0 = c_beg + lane; c0 < c_end; c0 += kWave * kBurst) {
@@ -125,8 +125,9 @@ __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
 // (8 bytes per chunk) then one scale per 128-channel block.
 __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const u32x4 *__restrict__ x, int nvec, int slice, const int32_t *__restrict__ dest, int D,
-    uint8_t *__restrict__ recv, float *__restrict__ scales, const int32_t *__restrict__ totals,
-    const int32_t *lo_p, const int32_t *hi_p, int64_t T)
+    uint8_t *__restrict__ recv, float *__restrict__ scales, int64_t cap,
+    unsigned long long *viol, const int32_t *__restrict__ totals, const int32_t *lo_p,
+    const int32_t *hi_p, int64_t T)
 {
     extern __shared__ u32x4 s_codes[];   // slice/2 vectors of 16 codes
     const int64_t t = item_index();
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
     const int row_blk = nvec >> 4;         // scales per row
     for (int d = wave; d < D; d += kWaves) {
         const int64_t r = dest[t * D + d];
-        if (r < lo || r >= hi)
+        if (r < lo || r >= hi || !in_bounds(r, cap, viol))
             continue;
         u32x4 *dst = (u32x4 *)(recv) + r * row_vec + (c_beg >> 1);
         for (int c0 = lane; c0 < nq; c0 += kWave * kBurstFp8) {
@@ -197,7 +198,8 @@ __global__ void f32_to_e4m3_kernel(const float *__restrict__ in, uint8_t *__rest
 }  // namespace
 
 hipError_t launch_dispatch_bf16(const Geometry &g, const epx_layout &L, const void *x,
-                                int32_t hidden, void *recv, int group, hipStream_t stream)
+                                int32_t hidden, void *recv, int64_t cap, int group,
+                                hipStream_t stream)
 {
     const int32_t *lo_p = group < 0 ? nullptr : L.group_offset + group * g.R;
     const int32_t *hi_p = group < 0 ? nullptr : L.group_offset + (group + 1) * g.R;
@@ -207,13 +209,13 @@ hipError_t launch_dispatch_bf16(const Geometry &g, const epx_layout &L, const vo
     const int slice = slice_width(g.T, nvec, kWave, 1 << 30, 2048);
     const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
     launch(dispatch_bf16_kernel, grid, dim3(kThreads), 0, stream, (const u32x4 *)x,
-                       nvec, slice, dest, D, (u32x4 *)recv, (const int32_t *)L.totals, lo_p,
-                       hi_p, (int64_t)g.T);
+                       nvec, slice, dest, D, (u32x4 *)recv, cap, g.viol, (const int32_t *)L.totals,
+                       lo_p, hi_p, (int64_t)g.T);
     return hipGetLastError();
 }
 
 hipError_t launch_dispatch_fp8(const Geometry &g, const epx_layout &L, const void *x,
-                               int32_t hidden, void *recv, float *scales, int group,
+                               int32_t hidden, void *recv, float *scales, int64_t cap, int group,
                                hipStream_t stream)
 {
     const int32_t *lo_p = group < 0 ? nullptr : L.group_offset + group * g.R;
@@ -231,8 +233,8 @@ hipError_t launch_dispatch_fp8(const Geometry &g, const epx_layout &L, const voi
     const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
     const size_t lds = (size_t)slice * 8 + (size_t)(slice / 16) * sizeof(float);
     launch(dispatch_fp8_kernel, grid, dim3(kThreads), lds, stream, (const u32x4 *)x,
-                       nvec, slice, dest, D, (uint8_t *)recv, scales, (const int32_t *)L.totals,
-                       lo_p, hi_p, (int64_t)g.T);
+                       nvec, slice, dest, D, (uint8_t *)recv, scales, cap, g.viol,
+                       (const int32_t *)L.totals, lo_p, hi_p, (int64_t)g.T);
     return hipGetLastError();
 }
 

@@ -316,12 +316,13 @@ __device__ void token_rows(int t, const int32_t *__restrict__ idx, const Geometr
     if (blockIdx.y == 0) {
         if (tid < g.k) {
             L.slot[pt + tid] = s_slot[tid];
-            L.row_token[s_slot[tid]] = t;
+            if (in_bounds(s_slot[tid], pair_rows(g), g.viol))
+                L.row_token[s_slot[tid]] = t;
         }
         if (g.relay && tid < g.H) {
             const int h = tid, r = s_rrow[h];
             L.relay_slot[(int64_t)t * g.H + h] = r;
-            if (r >= 0) {
+            if (r >= 0 && in_bounds(r, relay_rows_cap(g), g.viol)) {
                 L.relay_token[r] = t;
                 uint32_t mask = 0;
                 for (int j = 0; j < g.k; ++j) {
@@ -352,7 +353,7 @@ __device__ void token_rows(int t, const int32_t *__restrict__ idx, const Geometr
         const int p_beg = c_beg + part * len, p_end = min(c_end, p_beg + len);
         for (int d = wave / wpr; d < D; d += kFWaves / wpr) {
             const int64_t r = dst_rows[d];
-            if (r < 0)
+            if (r < 0 || !in_bounds(r, g.cap, g.viol))
                 continue;
             u32x4 *dst = (u32x4 *)recv + r * nvec;
             for (int c0 = p_beg + lane; c0 < p_end; c0 += kWave * kFBurst) {
@@ -386,7 +387,7 @@ __device__ void token_rows(int t, const int32_t *__restrict__ idx, const Geometr
     const int q_beg = part * len, q_end = min(nq, q_beg + len);
     for (int d = wave / wpr; d < D; d += kFWaves / wpr) {
         const int64_t r = dst_rows[d];
-        if (r < 0)
+        if (r < 0 || !in_bounds(r, g.cap, g.viol))
             continue;
         u32x4 *dst = (u32x4 *)recv + r * row_vec + (c_beg >> 1);
         for (int c0 = q_beg + lane; c0 < q_end; c0 += kWave * kFBurst) {

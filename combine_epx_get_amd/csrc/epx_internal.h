@@ -18,6 +18,26 @@ constexpr int kMaxHosts = 64;
 constexpr int kMaxRanksPerHost = 32;
 constexpr int kFp8Block = 128;       // channels per fp8 scale
 
+// Bounds-checked builds (libepx_checked.so, compiled with EPX_CHECKED):
+// every row index that a kernel computes, or reads from a layout, is checked
+// against the buffer it addresses before the access; an index out of bounds
+// skips the access and is counted in a device counter that
+// epx_checked_violations reads. In the release build the checks compile
+// away (in_bounds is constant true).
+#ifdef EPX_CHECKED
+constexpr bool kChecked = true;
+#else
+constexpr bool kChecked = false;
+#endif
+
+__device__ __forceinline__ bool in_bounds(int64_t i, int64_t n, unsigned long long *viol)
+{
+    if (!kChecked || (uint64_t)i < (uint64_t)n)
+        return true;
+    atomicAdd(viol, 1ull);
+    return false;
+}
+
 // Division by a divisor fixed per call, as a multiply-high: q = umulhi(n, m)
 // with m = ceil(2^32 / d) is exact whenever n * d < 2^32 (the error n*(m -
 // 2^32/d)/2^32 stays below 1/d). Every use here has n, d <= 4096.
@@ -48,7 +68,17 @@ struct Geometry {
     int32_t m;       // expert groups (1: none)
     int32_t epg;     // experts per rank in one group: epr / m
     FastDiv div_epr, div_rph, div_k;
+    unsigned long long *viol;   // violation counter (checked builds; else null)
+    int64_t cap;     // rows of the call's destination buffer (recv) for layout kernels
+                     // that also dispatch (checked builds)
 };
+
+// Rows of per-expert and relay layout arrays: T*k and T*min(k, H).
+__host__ __device__ inline int64_t pair_rows(const Geometry &g) { return (int64_t)g.T * g.k; }
+__host__ __device__ inline int64_t relay_rows_cap(const Geometry &g)
+{
+    return (int64_t)g.T * (g.k < g.H ? g.k : g.H);
+}
 
 // One workgroup per item (token or row) for any item count: item i runs as
 // blockIdx.x = i mod kGridX, blockIdx.z = i / kGridX (blockIdx.y stays free
@@ -104,10 +134,12 @@ inline void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
 hipError_t launch_layout(const Geometry &g, const int32_t *idx, const epx_layout &L,
                          hipStream_t stream);
 // group < 0: every destination; else only group `group`'s rows.
+// cap: rows of recv (and of the scales).
 hipError_t launch_dispatch_bf16(const Geometry &g, const epx_layout &L, const void *x,
-                                int32_t hidden, void *recv, int group, hipStream_t stream);
+                                int32_t hidden, void *recv, int64_t cap, int group,
+                                hipStream_t stream);
 hipError_t launch_dispatch_fp8(const Geometry &g, const epx_layout &L, const void *x,
-                               int32_t hidden, void *recv, float *scales, int group,
+                               int32_t hidden, void *recv, float *scales, int64_t cap, int group,
                                hipStream_t stream);
 // Layout and dispatch in one launch; false (nothing launched) when the batch
 // is too large for it. *err receives the launch status otherwise.
@@ -121,20 +153,24 @@ bool launch_layout_dispatch(const Geometry &g, const int32_t *idx, const epx_lay
 bool launch_layout_assign_dispatch(const Geometry &g, const int32_t *idx, const epx_layout &L,
                                    const void *x, int32_t hidden, bool fp8, void *recv,
                                    float *scales, hipStream_t stream, hipError_t *err);
-hipError_t launch_combine(const Geometry &g, const epx_layout &L, const void *y,
+// y_rows: rows of y.
+hipError_t launch_combine(const Geometry &g, const epx_layout &L, const void *y, int64_t y_rows,
                           const float *w, int32_t hidden, void *out, hipStream_t stream);
 hipError_t launch_combine_group(const Geometry &g, const epx_layout &L, int group,
-                                const void *y, const float *w, int32_t hidden, float *carry,
-                                void *out, hipStream_t stream);
+                                const void *y, int64_t y_rows, const float *w, int32_t hidden,
+                                float *carry, void *out, hipStream_t stream);
 hipError_t launch_f32_to_e4m3(const float *in, uint8_t *out, int64_t n, hipStream_t stream);
+// relay_cap, cap, y_rows, part_cap: rows of relay_rows, recv, y and partials.
 hipError_t launch_relay_fanout(const Geometry &g, const epx_layout &L, const void *relay_rows,
-                               const float *relay_scales, int64_t row_bytes, int nsc,
-                               void *recv, float *recv_scales, hipStream_t stream);
+                               const float *relay_scales, int64_t relay_cap, int64_t row_bytes,
+                               int nsc, void *recv, float *recv_scales, int64_t cap,
+                               hipStream_t stream);
 hipError_t launch_relay_partials(const Geometry &g, const epx_layout &L, const void *y,
-                                 const float *w, int32_t hidden, bool bf16_out, void *partials,
-                                 hipStream_t stream);
+                                 int64_t y_rows, const float *w, int32_t hidden, bool bf16_out,
+                                 void *partials, int64_t part_cap, hipStream_t stream);
 hipError_t launch_relay_finish(const Geometry &g, const epx_layout &L, const void *partials,
-                               bool bf16_in, int32_t hidden, void *out, hipStream_t stream);
+                               int64_t part_cap, bool bf16_in, int32_t hidden, void *out,
+                               hipStream_t stream);
 hipError_t launch_plan_swaps(int E, int R, int H, const int32_t *count, const int32_t *slot_in,
                              int tau, int32_t *slot_out, int32_t *load_before,
                              int32_t *load_after, int32_t *swaps, int32_t *host_bad,

@@ -105,6 +105,8 @@ __device__ __forceinline__ void relay_item(bool act, int t, int i, int h, const 
     }
     const int r = base + __popcll(bal & ((1ull << lane) - 1ull));
     L.relay_slot[(int64_t)t * g.H + h] = r;
+    if (!in_bounds(r, relay_rows_cap(g), g.viol))
+        return;   // checked builds only
     L.relay_token[r] = t;
     const int32_t *ids = s_idx + i * g.k, *hks = s_hk + i * g.k, *rks = s_rk + i * g.k;
     int32_t *fan = L.fanout_expert + (int64_t)r * g.k;
@@ -386,7 +388,8 @@ __device__ void assign_chunk(const int32_t *__restrict__ idx, const Geometry &g,
             const int rel = s_wc[wave * cs + e];
             const int row = s_eoff[e] + rel + before;
             L.slot[p0 + p] = row;
-            L.row_token[row] = t0 + g.div_k.div(p);
+            if (in_bounds(row, pair_rows(g), g.viol))
+                L.row_token[row] = t0 + g.div_k.div(p);
             if (before == 0)
                 s_wc[wave * cs + e] = rel + __popcll(peers);
         }
@@ -530,7 +533,7 @@ __global__ __launch_bounds__(kFusedThreads) void assign_copy_kernel(
         // a wave streams whole rows, 16 KiB per burst
         for (int d = wave; d < D; d += kFusedWaves) {
             const int r = s_rows[d];
-            if (r < 0)
+            if (r < 0 || !in_bounds(r, g.cap, g.viol))
                 continue;
             u32x4 *dst = (u32x4 *)recv + (int64_t)r * nvec;
             for (int c0 = c_beg + lane; c0 < c_end; c0 += kWave * kFusedBurst) {
@@ -560,7 +563,7 @@ __global__ __launch_bounds__(kFusedThreads) void assign_copy_kernel(
     const int nq = n >> 1, nblk = n >> 4, row_vec = nvec >> 1, row_blk = nvec >> 4;
     for (int d = wave; d < D; d += kFusedWaves) {
         const int r = s_rows[d];
-        if (r < 0)
+        if (r < 0 || !in_bounds(r, g.cap, g.viol))
             continue;
         u32x4 *dst = (u32x4 *)recv + (int64_t)r * row_vec + (c_beg >> 1);
         for (int c0 = lane; c0 < nq; c0 += kWave * kFusedBurstFp8) {
@@ -773,7 +776,8 @@ __global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
             const int rel = s_cnt[wave * cs + e];
             const int row = s_eoff[e] + rel + before;
             L.slot[p] = row;
-            L.row_token[row] = g.div_k.div(p);
+            if (in_bounds(row, pair_rows(g), g.viol))
+                L.row_token[row] = g.div_k.div(p);
             if (before == 0)
                 s_cnt[wave * cs + e] = rel + __popcll(peers);
         }

@@ -33,17 +33,21 @@ constexpr int kBurst = 16;   // fan-out: row vectors per lane loaded before its 
 
 // The fan-out list of relay row r in ascending j: (destination slot, j).
 // Returns its length; s_dst / s_j hold up to k entries. Every thread calls it.
+// (Checked builds drop slots at or past dst_rows, counted.)
 __device__ __forceinline__ int fanout_list(const epx_layout &L, int k, int64_t r, int t,
-                                           int32_t *s_dst, int32_t *s_j, int32_t *s_n)
+                                           int32_t *s_dst, int32_t *s_j, int32_t *s_n,
+                                           int64_t dst_rows, unsigned long long *viol)
 {
     if (threadIdx.x < kWave) {
         // k <= 64: one lane per j, compacted in j order with a ballot prefix
         const int j = threadIdx.x;
-        const bool on = j < k && L.fanout_expert[r * k + j] >= 0;
+        bool on = j < k && L.fanout_expert[r * k + j] >= 0;
+        const int o = on ? L.slot[(int64_t)t * k + j] : 0;
+        on = on && in_bounds(o, dst_rows, viol);
         const uint64_t bal = __ballot(on);
         if (on) {
             const int pos = __popcll(bal & ((1ull << j) - 1ull));
-            s_dst[pos] = L.slot[(int64_t)t * k + j];
+            s_dst[pos] = o;
             s_j[pos] = j;
         }
         if (j == 0)
@@ -56,7 +60,8 @@ __device__ __forceinline__ int fanout_list(const epx_layout &L, int k, int64_t r
 // Rows are row_vec 16-byte vectors; nsc float32 scales per row (fp8) or 0.
 __global__ __launch_bounds__(kThreads) void relay_fanout_kernel(
     const u32x4 *__restrict__ src, const float *__restrict__ src_sc, int row_vec, int nsc,
-    int slice, int k, epx_layout L, u32x4 *__restrict__ dst, float *__restrict__ dst_sc)
+    int slice, int k, epx_layout L, u32x4 *__restrict__ dst, float *__restrict__ dst_sc,
+    int64_t T, int64_t relay_cap, int64_t cap, unsigned long long *viol)
 {
     __shared__ int32_t s_dst[kMaxTopk], s_j[kMaxTopk], s_n;
     if (L.totals[3] != 0)
@@ -65,7 +70,12 @@ __global__ __launch_bounds__(kThreads) void relay_fanout_kernel(
     if (r >= L.totals[1])
         return;   // past the relay rows in use (also past the grid's last row)
     const int t = L.relay_token[r];
-    const int n = fanout_list(L, k, r, t, s_dst, s_j, &s_n);
+    if (kChecked && ((uint64_t)r >= (uint64_t)relay_cap || (uint64_t)t >= (uint64_t)T)) {
+        if (threadIdx.x == 0)
+            atomicAdd(viol, 1ull);   // checked builds: a relay row or token out of range
+        return;
+    }
+    const int n = fanout_list(L, k, r, t, s_dst, s_j, &s_n, cap, viol);
     const int c_beg = blockIdx.y * slice;
     const int c_end = min(row_vec, c_beg + slice);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -104,7 +114,8 @@ constexpr int kParBatch = 4;
 template <bool BF16_OUT>
 __global__ __launch_bounds__(kThreads) void relay_partials_kernel(
     const u32x4 *__restrict__ y, int nvec, int slice, const float *__restrict__ w, int k,
-    epx_layout L, void *__restrict__ partials)
+    epx_layout L, void *__restrict__ partials, int64_t T, int64_t part_cap, int64_t y_rows,
+    unsigned long long *viol)
 {
     __shared__ int32_t s_dst[kMaxTopk], s_j[kMaxTopk], s_n;
     __shared__ float s_w[kMaxTopk];
@@ -114,7 +125,12 @@ __global__ __launch_bounds__(kThreads) void relay_partials_kernel(
     if (r >= L.totals[1])
         return;   // past the relay rows in use (also past the grid's last row)
     const int t = L.relay_token[r];
-    const int n = fanout_list(L, k, r, t, s_dst, s_j, &s_n);
+    if (kChecked && ((uint64_t)r >= (uint64_t)part_cap || (uint64_t)t >= (uint64_t)T)) {
+        if (threadIdx.x == 0)
+            atomicAdd(viol, 1ull);   // checked builds: a relay row or token out of range
+        return;
+    }
+    const int n = fanout_list(L, k, r, t, s_dst, s_j, &s_n, y_rows, viol);
     if ((int)threadIdx.x < n)
         s_w[threadIdx.x] = w[(int64_t)t * k + s_j[threadIdx.x]];
     __syncthreads();
@@ -212,7 +228,7 @@ __device__ __forceinline__ void load_partial(const void *partials, int64_t r, in
 template <bool BF16_IN>
 __global__ __launch_bounds__(kThreads) void relay_finish_kernel(
     const void *__restrict__ partials, int nvec, int slice, int H, epx_layout L,
-    u32x4 *__restrict__ out, int64_t T)
+    u32x4 *__restrict__ out, int64_t T, int64_t part_cap, unsigned long long *viol)
 {
     __shared__ int32_t s_rows[kMaxHosts], s_n;
     const int64_t t = item_index();
@@ -220,7 +236,9 @@ __global__ __launch_bounds__(kThreads) void relay_finish_kernel(
         return;
     if (threadIdx.x < kWave) {
         const int h = threadIdx.x;
-        const int r = h < H ? L.relay_slot[t * H + h] : -1;
+        int r = h < H ? L.relay_slot[t * H + h] : -1;
+        if (r >= 0 && !in_bounds(r, part_cap, viol))
+            r = -1;   // checked builds: a partial row out of range (counted)
         const uint64_t bal = __ballot(r >= 0);
         if (r >= 0)
             s_rows[__popcll(bal & ((1ull << h) - 1ull))] = r;
@@ -289,48 +307,54 @@ int slices_for(int64_t rows, int nvec, int align, int target)
 }  // namespace
 
 hipError_t launch_relay_fanout(const Geometry &g, const epx_layout &L, const void *relay_rows,
-                               const float *relay_scales, int64_t row_bytes, int nsc,
-                               void *recv, float *recv_scales, hipStream_t stream)
+                               const float *relay_scales, int64_t relay_cap, int64_t row_bytes,
+                               int nsc, void *recv, float *recv_scales, int64_t cap,
+                               hipStream_t stream)
 {
-    const int64_t cap = (int64_t)g.T * (g.k < g.H ? g.k : g.H);
+    const int64_t rows = relay_rows_cap(g);   // relay rows of the layout (<= relay_cap)
     const int row_vec = (int)(row_bytes / 16);
-    const int slice = slices_for(cap, row_vec, kWave, 2048);
-    const dim3 grid = item_grid(cap, (row_vec + slice - 1) / slice);
+    const int slice = slices_for(rows, row_vec, kWave, 2048);
+    const dim3 grid = item_grid(rows, (row_vec + slice - 1) / slice);
     launch(relay_fanout_kernel, grid, dim3(kThreads), 0, stream,
                        (const u32x4 *)relay_rows, relay_scales, row_vec, nsc, slice, g.k, L,
-                       (u32x4 *)recv, recv_scales);
+                       (u32x4 *)recv, recv_scales, (int64_t)g.T,
+                       relay_cap < rows ? relay_cap : rows, cap, g.viol);
     return hipGetLastError();
 }
 
 hipError_t launch_relay_partials(const Geometry &g, const epx_layout &L, const void *y,
-                                 const float *w, int32_t hidden, bool bf16_out, void *partials,
-                                 hipStream_t stream)
+                                 int64_t y_rows, const float *w, int32_t hidden, bool bf16_out,
+                                 void *partials, int64_t part_cap, hipStream_t stream)
 {
-    const int64_t cap = (int64_t)g.T * (g.k < g.H ? g.k : g.H);
+    const int64_t rows = relay_rows_cap(g);
     const int nvec = hidden / 8;
-    const int slice = slices_for(cap, nvec, kWave, 2048);
-    const dim3 grid = item_grid(cap, (nvec + slice - 1) / slice);
+    const int slice = slices_for(rows, nvec, kWave, 2048);
+    const dim3 grid = item_grid(rows, (nvec + slice - 1) / slice);
+    const int64_t pc = part_cap < rows ? part_cap : rows;
     if (bf16_out)
         launch(relay_partials_kernel<true>, grid, dim3(kThreads), 0, stream,
-                           (const u32x4 *)y, nvec, slice, w, g.k, L, partials);
+                           (const u32x4 *)y, nvec, slice, w, g.k, L, partials, (int64_t)g.T, pc,
+                           y_rows, g.viol);
     else
         launch(relay_partials_kernel<false>, grid, dim3(kThreads), 0, stream,
-                           (const u32x4 *)y, nvec, slice, w, g.k, L, partials);
+                           (const u32x4 *)y, nvec, slice, w, g.k, L, partials, (int64_t)g.T, pc,
+                           y_rows, g.viol);
     return hipGetLastError();
 }
 
 hipError_t launch_relay_finish(const Geometry &g, const epx_layout &L, const void *partials,
-                               bool bf16_in, int32_t hidden, void *out, hipStream_t stream)
+                               int64_t part_cap, bool bf16_in, int32_t hidden, void *out,
+                               hipStream_t stream)
 {
     const int nvec = hidden / 8;
     const int slice = slices_for(g.T, nvec, kWave, 2048);
     const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
     if (bf16_in)
         launch(relay_finish_kernel<true>, grid, dim3(kThreads), 0, stream, partials,
-                           nvec, slice, g.H, L, (u32x4 *)out, (int64_t)g.T);
+                           nvec, slice, g.H, L, (u32x4 *)out, (int64_t)g.T, part_cap, g.viol);
     else
         launch(relay_finish_kernel<false>, grid, dim3(kThreads), 0, stream, partials,
-                           nvec, slice, g.H, L, (u32x4 *)out, (int64_t)g.T);
+                           nvec, slice, g.H, L, (u32x4 *)out, (int64_t)g.T, part_cap, g.viol);
     return hipGetLastError();
 }
 

@@ -16,7 +16,10 @@ from typing import Dict, List, Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libepx.so")
+# The release library, or the one EPX_LIBRARY names (e.g. the bounds-checked
+# libepx_checked.so built beside it).
+_LIB_PATH = os.environ.get("EPX_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "libepx.so")
 if not os.path.exists(_LIB_PATH):
     raise ImportError(f"{_LIB_PATH} is not built; run `python -m combine_epx_get_amd.build`")
 _lib = ctypes.CDLL(_LIB_PATH)
@@ -74,12 +77,14 @@ _lib.epx_combine_group.argtypes = [ctypes.POINTER(epx_problem), ctypes.POINTER(e
 _lib.epx_plan_swaps.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32,
                                 _P, _P, _P, _P, _P, _P]
 _lib.epx_time_next_call.argtypes = [_P, _P]
+_lib.epx_checked_violations.argtypes = [ctypes.POINTER(ctypes.c_int64), _P]
 _lib.epx_status_string.argtypes = [ctypes.c_int]
 _lib.epx_status_string.restype = ctypes.c_char_p
 for _f in ("epx_layout_sizes", "epx_get_layout", "epx_dispatch", "epx_combine", "epx_read_error",
            "epx_f32_to_e4m3", "epx_relay_fanout", "epx_combine_relay_partials",
            "epx_combine_relay_finish", "epx_plan_swaps", "epx_dispatch_group", "epx_combine_group",
-           "epx_layout_dispatch", "epx_time_next_call", "epx_layout_dispatch_noalloc"):
+           "epx_layout_dispatch", "epx_time_next_call", "epx_layout_dispatch_noalloc",
+           "epx_checked_violations"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.epx_abi_version.restype = ctypes.c_int32
 NARRAYS = len(LAYOUT_FIELDS)
@@ -284,6 +289,14 @@ def epx_time_next_call(start_event: Optional[int], stop_event: Optional[int]) ->
     from this thread (start: its first kernel's start, stop: its last kernel's
     end); None, None disarms."""
     _check(_lib.epx_time_next_call(start_event, stop_event), "epx_time_next_call")
+
+
+def epx_checked_violations(stream=None) -> int:
+    """Bounds-checked library only: accesses its checks skipped since the last
+    call (synchronises the stream and resets the count)."""
+    n = ctypes.c_int64(-1)
+    _check(_lib.epx_checked_violations(ctypes.byref(n), _stream(stream)), "epx_checked_violations")
+    return int(n.value)
 
 
 def epx_f32_to_e4m3(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:

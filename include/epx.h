@@ -356,6 +356,19 @@ EPX_API epx_status epx_plan_swaps(int32_t num_experts, int32_t num_ranks, int32_
  * number in *bad_count if not NULL). For tests and debugging. */
 EPX_API epx_status epx_read_error(const epx_layout *layout, int32_t *bad_count, void *stream);
 
+/* Bounds-checked build (libepx_checked.so, the same sources compiled with
+ * EPX_CHECKED; a debugging aid, not the product path): every row index that a
+ * kernel computes, or reads from a layout, is checked against the buffer it
+ * addresses (the capacities passed to the call; T*k and T*min(k, H) for the
+ * layout's own arrays) before the access, and an index out of bounds skips
+ * the access and is counted on the device (once per lane that skips, so the
+ * count is not a number of rows). This call synchronises `stream`,
+ * returns the count accumulated on the current device since the last call in
+ * *count and resets it. In the release build (libepx.so) nothing is checked:
+ * it returns EPX_ERR_ARG and *count = -1. Errors: EPX_ERR_ARG (count NULL, or
+ * a release build), EPX_ERR_DEVICE. */
+EPX_API epx_status epx_checked_violations(int64_t *count, void *stream);
+
 /* Elementwise float32 -> E4M3FN with the rounding and saturation that the
  * fp8 dispatch uses (in [n] -> out [n], device arrays). A diagnostic entry
  * point for checking the conversion exhaustively. */

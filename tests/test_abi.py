@@ -244,6 +244,21 @@ def test_noalloc_entry_host_checks(epx):
     assert epx.epx_layout_sizes(lb)[epx.LAYOUT_FIELDS.index("workspace")] * 4 < (1 << 20)
 
 
+def test_release_build_checks_nothing(epx):
+    """epx_checked_violations is for the bounds-checked build; the release
+    library refuses it on the host (count -1), before any HIP call."""
+    n = ctypes.c_int64(7)
+    assert epx._lib.epx_checked_violations(ctypes.byref(n), None) == 1 and n.value == -1
+    assert epx._lib.epx_checked_violations(None, None) == 1
+
+
+def test_checked_library_exports_the_same_symbols(epx):
+    lib = os.path.join(ROOT, "combine_epx_get_amd", "libepx_checked.so")
+    out = os.popen(f"nm -D --defined-only {lib}").read()
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(declared_functions())
+
+
 def test_binding_rejects_wrong_tensors(epx):
     import torch
     p = epx.make_problem(4, 2, 16, 4, 2)

@@ -217,6 +217,12 @@ int main()
     EXPECT(epx_time_next_call(A, nullptr), EPX_ERR_ARG);
     EXPECT(epx_time_next_call(nullptr, A), EPX_ERR_ARG);
     EXPECT(epx_time_next_call(nullptr, nullptr), EPX_OK);
+    {
+        int64_t n = 5;
+        EXPECT(epx_checked_violations(&n, nullptr), EPX_ERR_ARG);   // release build
+        EXPECT(n, -1);
+        EXPECT(epx_checked_violations(nullptr, nullptr), EPX_ERR_ARG);
+    }
     EXPECT(epx_abi_version(), EPX_ABI_VERSION);
     for (int code = 0; code <= 6; ++code)
         EXPECT(std::strlen(epx_status_string((epx_status)code)) > 0, 1);
