@@ -6,8 +6,8 @@ bounds skips the access and is counted (epx_checked_violations).
 
 * The parity cases (layout, dispatch in both modes and payloads, the fused
   call at decode and large sizes, combine, the relay receive side, expert
-  groups) run through the checked library: results bit-exact against the
-  oracle and not one violation.
+  groups, a third of the seeded random geometries) run through the checked
+  library: results bit-exact against the oracle and not one violation.
 * A layout made for a larger problem, used with a smaller one, yields rows
   past the declared capacities. The buffers are allocated at the larger
   problem's size, so each skipped access would still have landed inside an
@@ -28,6 +28,7 @@ import oracle
 from combine_epx_get_amd import workloads as W
 from tests import test_parity_fused_gpu as TF
 from tests import test_parity_gpu as TP
+from tests import test_parity_random_gpu as TRG
 from tests import test_parity_relay_gpu as TR
 
 pytestmark = pytest.mark.gpu
@@ -101,6 +102,35 @@ def test_checked_groups_without_violations(epxc):
         epxc.epx_combine_group(p, L, g, y, wts, carry, out)
     ora = oracle.layout_grouped(idx, E, R, m)
     assert np.array_equal(TP._bits(recv), x[ora["row_token"]])
+    assert epxc.epx_checked_violations() == 0
+
+
+RANDOM = TRG.CASES[::3]
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[f"c{c['seed']}-T{c['T']}k{c['k']}E{c['E']}R{c['R']}H{c['H']}h{c['hidden']}"
+                                              for c in RANDOM])
+def test_checked_random_geometries_without_violations(epxc, case):
+    """A third of the seeded random geometries (empty batches, k up to 64,
+    up to 64 hosts, duplicate ids) through the checked library: every call,
+    the relay receive side included, bit-exact and in bounds."""
+    c = case
+    print(f"[checked random] {c}", flush=True)
+    rng = np.random.Generator(np.random.PCG64(5000 + c["seed"]))
+    T, k, E, R, H, s, h = c["T"], c["k"], c["E"], c["R"], c["H"], c["s"], c["hidden"]
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, h), dtype=np.float32))
+    if c["dup"]:
+        idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    else:
+        idx = W.draw_routing(rng, T, E, k, c["routing"], 1.1)
+    w = W.draw_gate_weights(rng, T, k)
+    dtypes = ("bf16", "fp8") if h % 128 == 0 else ("bf16",)
+    for relay in (False, True):
+        for dt in dtypes:
+            TP.run_case(epxc, x, idx, w, E, R, H, s, relay, dt, f"checked {c}/relay={relay}/{dt}")
+            TF.run_fused(epxc, x, idx, E, R, H, s, relay, dt, what=f"checked {c}/relay={relay}/fused {dt}")
+    if T > 0:
+        TR.run_relay_case(epxc, x, idx, w, E, R, H, s, f"checked relay {c}")
     assert epxc.epx_checked_violations() == 0
 
 
