@@ -36,8 +36,11 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
   plan_swaps     -- the worked example of digest Figure 2(b) (160/100 -> 130/130);
                     optimality of every chosen swap by enumeration; pairing,
                     threshold and conservation invariants.
-  relay row order, zero-block rule, fma order: parity unpinned by the pages
-                    (fixed by the readings recorded in the design notes).
+  Where the pages leave a choice open (relay row order, the all-zero block,
+  the fma order of combine), the oracle takes the reading recorded in the
+  design notes, and tests pin that reading: the row order by brute force, the
+  all-zero and signed-zero blocks by exact cases, the fma order by exact order
+  cases and planted mutants (tests/test_oracle_mutants.py).
 """
 from __future__ import annotations
 
