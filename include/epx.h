@@ -21,8 +21,9 @@
  * Conventions for every call:
  *  - Every array argument is a DEVICE pointer the caller allocated; the
  *    library allocates nothing and frees nothing. Its only state is the
- *    static scratch array of epx_layout_dispatch_noalloc (one per GPU) and
- *    the per-thread measurement hook of epx_time_next_call.
+ *    static scratch array of epx_layout_dispatch_noalloc (one per GPU), the
+ *    per-thread measurement hook of epx_time_next_call and, in the
+ *    bounds-checked build only, a device counter of skipped accesses.
  *    Activation pointers (x, recv, y, out) must be 16-byte aligned.
  *  - Calls are asynchronous and ordered on the HIP stream passed as `stream`
  *    (a hipStream_t; NULL = the null stream). No call synchronises the host,
