@@ -9,7 +9,9 @@
 // rows*h*2 bytes out, an HBM-bound scatter dominated by writes.
 //
 // Launch shape: one workgroup per (token, column slice); slices exist only to
-// give small batches enough workgroups. Each wave streams whole destination
+// give small batches enough workgroups. Large batches whose tokens have
+// fewer rows than a workgroup has waves give every wave a token of its own
+// instead (below). Each wave streams whole destination
 // rows (waves take the token's rows round-robin) in bursts of 16 KiB: every
 // lane loads 16 x 16 bytes of the token row (L2 serves the repeats), all in
 // flight together, and stores them with nontemporal 16-byte stores. Writing
@@ -51,18 +53,54 @@ __device__ __forceinline__ void row_range(const int32_t *lo_p, const int32_t *hi
     }
 }
 
+// wave_tokens != 0: every wave takes a token of its own (kWaves tokens per
+// workgroup, one column slice), loads its row once and stores it to all of
+// the token's D <= 64 rows; the launch uses it only for whole rows of one
+// burst, no group range, many tokens and few rows per token.
 __global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
     const u32x4 *__restrict__ x, int nvec, int slice, const int32_t *__restrict__ dest, int D,
     u32x4 *__restrict__ recv, int64_t cap, unsigned long long *viol,
-    const int32_t *__restrict__ totals, const int32_t *lo_p, const int32_t *hi_p, int64_t T)
+    const int32_t *__restrict__ totals, const int32_t *lo_p, const int32_t *hi_p, int64_t T,
+    int wave_tokens)
 {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    if (wave_tokens) {
+        const int64_t tw = item_index() * kWaves + wave;
+        if (tw >= T)
+            return;   // past the last token (no barrier below)
+        const u32x4 *xw = x + tw * nvec;
+        u32x4 v[kBurst];
+#pragma unroll
+        for (int i = 0; i < kBurst; ++i) {
+            const int c = lane + i * kWave;
+            if (c < nvec)
+                v[i] = xw[c];
+        }
+        // the error word and all destinations load beside the row
+        const int bad = totals[3];
+        const int rl = lane < D ? dest[tw * D + lane] : -1;
+        if (bad != 0)
+            return;   // the layout saw out-of-range expert ids: its rows are undefined
+        for (int d = 0; d < D; ++d) {
+            const int64_t r = __shfl(rl, d);
+            if (r < 0 || !in_bounds(r, cap, viol))
+                continue;   // relay: no row for this host
+            u32x4 *dst = recv + r * nvec;
+#pragma unroll
+            for (int i = 0; i < kBurst; ++i) {
+                const int c = lane + i * kWave;
+                if (c < nvec)
+                    __builtin_nontemporal_store(v[i], dst + c);
+            }
+        }
+        return;
+    }
     const int64_t t = item_index();
     if (t >= T)
         return;   // past the last token
     int lo, hi;
     const int c_beg = blockIdx.y * slice;
     const int c_end = min(nvec, c_beg + slice);
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const u32x4 *xr = x + t * nvec;
     if (c_end - c_beg <= kWave * kBurst) {
         // The slice fits one burst: each wave loads it once, together with
@@ -206,11 +244,21 @@ hipError_t launch_dispatch_bf16(const Geometry &g, const epx_layout &L, const vo
     const int32_t *dest = g.relay ? L.relay_slot : L.slot;
     const int D = g.relay ? g.H : g.k;
     const int nvec = hidden / 8;
-    const int slice = slice_width(g.T, nvec, kWave, 1 << 30, 2048);
-    const dim3 grid = item_grid(g.T, (nvec + slice - 1) / slice);
+    // A wave per token where a token has fewer rows than a workgroup has
+    // waves (relay to at most 3 hosts), so that no wave idles, when rows fit
+    // one burst and tokens are many. Measured on MI355X, 4096 x 7168, relay
+    // to 2 hosts: 24.9-25.8 us against 26.2-26.4 for a workgroup per token
+    // (two boxes); with 4 rows per token the two shapes are even, and with
+    // top-8 per-expert rows the workgroup per token is faster warm (92.8
+    // against 95.8 us over five rounds on one box; 2 us slower after a cache
+    // flush).
+    const bool wave_tokens = lo_p == nullptr && nvec <= kWave * kBurst && g.T >= 2048 && D < kWaves;
+    const int slice = wave_tokens ? nvec : slice_width(g.T, nvec, kWave, 1 << 30, 2048);
+    const dim3 grid = wave_tokens ? item_grid((g.T + kWaves - 1) / kWaves, 1)
+                                  : item_grid(g.T, (nvec + slice - 1) / slice);
     launch(dispatch_bf16_kernel, grid, dim3(kThreads), 0, stream, (const u32x4 *)x,
                        nvec, slice, dest, D, (u32x4 *)recv, cap, g.viol, (const int32_t *)L.totals,
-                       lo_p, hi_p, (int64_t)g.T);
+                       lo_p, hi_p, (int64_t)g.T, (int)wave_tokens);
     return hipGetLastError();
 }
 
