@@ -174,6 +174,8 @@ SHAPES = [
     (1500, 24, 96, 12, 3, 7, 128, "zipf"),      # k = 24: 42-token chunks, 36 workgroups
     (8200, 8, 256, 32, 4, 5, 128, "zipf"),      # 65 600 pairs: 257 chunk workgroups, a ragged last chunk
     (8192, 8, 256, 16, 2, 3, 128, "uniform"),   # 65 536 pairs: 256 full chunks
+    (2051, 6, 48, 6, 3, 4, 1000, "zipf"),       # relay to 3 hosts, a wave per token, 3 tokens in the last workgroup
+    (2049, 2, 8, 4, 1, 1, 7168, "uniform"),     # relay to 1 host, a wave per token, 1 token in the last workgroup
 ]
 
 
