@@ -191,7 +191,8 @@ EPX_API epx_status epx_get_layout(const epx_problem *p, const int32_t *topk_idx,
  * (HOST_RELAY); other rows of recv are left untouched. The layout must come
  * from epx_get_layout (or epx_layout_dispatch) with the same problem, ordered
  * before this call; the host cannot check its contents, and a layout made
- * for another problem can hold rows past capacity_rows. Errors: EPX_ERR_ARG
+ * for another problem can hold rows past capacity_rows (the bounds-checked
+ * build skips and counts such rows, see epx_checked_violations). Errors: EPX_ERR_ARG
  * (dtype, hidden, pointers, 16-byte alignment), EPX_ERR_CAPACITY (recv too
  * small); after a layout that saw bad ids nothing is written. */
 EPX_API epx_status epx_dispatch(const epx_problem *p, const epx_layout *layout, const void *x,
