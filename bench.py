@@ -198,7 +198,7 @@ def ingest_trace(stats_csv: str, tag: str, command: str) -> str:
     out = [f"# {tag}: rocprofv3 kernel trace", "",
            f"sources_hash: {kernel_sources_hash()} (every file of combine_epx_get_amd/csrc; bench.py "
            f"reports these averages only while the sources hash to it)", "",
-           "Command (on the GPU box; $REPO is the repository root):", "", "    " + command, "",
+           "Command ($REPO is the repository root, run on an MI355X):", "", "    " + command, "",
            "| kernel | calls | average µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| {short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
