@@ -22,8 +22,8 @@
 // 4 KiB bursts took 118.7 us after a cache flush, 16 KiB bursts 109.2 us
 // (95.5 and 96.0 us with warm caches).
 //
-// The fp8 variant is the BF16-to-FP8 conversion that dispatch performs
-// (digest section 3.1): per token and 128-channel block, scale = amax/448 and
+// The fp8 variant quantises bf16 to fp8 inside the dispatch (digest section
+// 3.1): per token and 128-channel block, scale = amax/448 and
 // code = E4M3(x / scale), the float32 quotient correctly rounded, then
 // rounded to nearest even in E4M3. The workgroup quantises its slice once into LDS (a
 // 16-lane group owns one 128-channel block: 8 bf16 per lane, block maximum by

@@ -5,9 +5,9 @@
 // and of every (token, host) relay copy. The copies per expert and per host
 // are the quantities the digest "Balancing and Beyond: Communication-Centric
 // Optimizations in Expert Parallelism" reasons about (section 2: the busiest
-// expert sets the time; section 3.2: one network copy per remote host); the
-// per-rank token counts are those of the DeepEP issue "[GH-ISSUE #250]
-// Profiling when rank unbalance".
+// expert sets the time; section 3.2: a single cross-host copy to each remote
+// host); the per-rank token counts are those of the DeepEP issue
+// "[GH-ISSUE #250] Profiling when rank unbalance".
 //
 // Row order: per-expert rows by (expert, token, j) -- with expert groups by
 // (group, expert, token, j); relay rows by (host, token). Positions come

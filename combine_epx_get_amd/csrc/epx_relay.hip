@@ -1,11 +1,11 @@
 // epx_relay.hip -- receive side of the host relay and the two-level combine.
 //
 // Mode 2 of the digest "Balancing and Beyond: Communication-Centric
-// Optimizations in Expert Parallelism" (section 3.2, Figure 3): a token's
-// copy crosses to the same-index GPU of each destination host once and is
-// fanned out there to the token's experts on that host; on the way back that
-// GPU sums its experts' results and returns one partial per token, which the
-// source sums over the hosts.
+// Optimizations in Expert Parallelism" (section 3.2, Figure 3): a token goes
+// to each destination host once, to the GPU there whose local index equals
+// the sender's, which hands it on to the token's experts on that host; the
+// results come back the same way, pre-summed over that host's experts into
+// one partial per token, and the source adds the partials of its hosts.
 //
 //   relay_fanout:   relay row r -> per-expert rows slot[t, j] of every j with
 //                   fanout_expert[r, j] >= 0 (bf16 rows, or fp8 codes +

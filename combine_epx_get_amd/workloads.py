@@ -7,7 +7,7 @@ any of the method's code.
 
 Shapes follow the workloads of "Balancing and Beyond: Communication-Centric
 Optimizations in Expert Parallelism" (research digest, section 5: DeepSeek-R1
-with 256 experts, top-8, hidden 7168; decode at up to 128 tokens per GPU,
+with 256 experts, top-8, hidden 7168; decode with at most 128 tokens on a GPU,
 section 1) and of "Poor HybridEP performance on dual-node 16x B300 GPUs"
 (4096 tokens per rank, hidden 7168, top-8). The production routing traces of
 the digest (section 2, Figure 2) are not available; uniform and Zipf-skewed

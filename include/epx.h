@@ -70,7 +70,7 @@ typedef enum {
 #define EPX_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /* Transport layout of dispatch (digest section 3.2, Figure 3).
- * PER_EXPERT: one copy of a token per destination expert (DeepEP's Mode 1).
+ * PER_EXPERT: a token row for each of its destination experts (DeepEP's Mode 1).
  * HOST_RELAY: one copy per destination host, addressed to the same-index GPU
  *             on that host, plus an index to fan it out there (Mode 2 with
  *             de-redundancy). */
@@ -288,7 +288,7 @@ EPX_API epx_status epx_combine_group(const epx_problem *p, const epx_layout *lay
                                      void *out, void *stream);
 
 /* ---- Host relay, receive side and two-level combine (digest section 3.2,
- * Mode 2 with de-redundancy, Figure 3). Problem mode must be HOST_RELAY.
+ * Mode 2, Figure 3). Problem mode must be HOST_RELAY.
  * C = T * min(k, H) is the relay row capacity. ---- */
 
 /* Fan-out at the same-index GPU of a host: every relay row r (token t) is
@@ -334,8 +334,9 @@ EPX_API epx_status epx_combine_relay_finish(const epx_problem *p, const epx_layo
  * lightest (i < (R/H)/2; an odd middle rank stays unpaired). Each pair takes
  * the single expert exchange that gives the smallest new pair maximum (ties:
  * smaller slot of the heavier rank, then smaller slot of the lighter rank)
- * and applies it only if the maximum falls by at least max(tau, 1) tokens;
- * tau is the swap cost in token units (weight-move time over per-token time).
+ * and applies it only when the pair's maximum drops by max(tau, 1) tokens
+ * or more; tau is the swap cost in token units (weight-move time over
+ * per-token time).
  *
  * Device arrays: expert_count int32 [E] (non-negative, total < 2^31);
  * slot_expert_in / slot_expert_out int32 [E] (distinct buffers);

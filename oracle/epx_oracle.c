@@ -11,9 +11,10 @@
  *
  *  - Layout: counts per expert, per rank and per host, prefix offsets and the
  *    position of every (token, expert) copy. The digest "Balancing and
- *    Beyond: Communication-Centric Optimizations in Expert Parallelism" sends
- *    each token to its top-k experts (section 1) and defines the imbalance
- *    ratio as the busiest expert's tokens over the layer mean (section 2);
+ *    Beyond: Communication-Centric Optimizations in Expert Parallelism"
+ *    routes every token to k experts chosen for it (section 1) and measures
+ *    imbalance as the largest expert count divided by the mean count
+ *    (section 2);
  *    the DeepEP issue "[GH-ISSUE #250] Profiling when rank unbalance" counts
  *    the tokens each rank receives (the maintainer's estimate and the
  *    follow-up question).

@@ -173,7 +173,7 @@ def test_layout_invariants_full_size(name):
     assert np.array_equal((rs >= 0).sum(1), distinct)
     used = rs[rs >= 0]
     assert np.array_equal(np.sort(used), np.arange(distinct.sum()))
-    # imbalance ratio: busiest expert over the layer mean (digest section 2)
+    # imbalance ratio = max expert count / mean expert count (digest section 2)
     ratio = lay["totals"][2] / (T * k / w.num_experts)
     assert ratio >= 1.0
     assert lay["totals"][2] == lay["expert_count"].max()

@@ -4,7 +4,7 @@ Bar: bit-exact against the oracle (layout arrays, bf16 rows, fp8 codes and
 scales) and, array by array, identical to epx_get_layout followed by
 epx_dispatch on arrays pre-filled with the same sentinel, so that an entry
 one path writes and the other leaves alone also fails. Decode batches of
-the digest "Balancing and Beyond" (section 1: up to 128 tokens per GPU;
+the digest "Balancing and Beyond" (section 1: at most 128 tokens on a GPU;
 section 5: 256 experts, top-8, hidden 7168) take the fused kernel; the
 sizes past its limits (T > 1024, T*k > 4096, E > 512, LDS) take the two
 launches inside the same call and must give the same results too.
