@@ -250,8 +250,8 @@ hipError_t launch_dispatch_bf16(const Geometry &g, const epx_layout &L, const vo
     // to 2 hosts: 24.9-25.8 us against 26.2-26.4 for a workgroup per token
     // (two machines); with 4 rows per token the two shapes are even; with
     // top-8 per-expert rows the workgroup per token is faster warm (92.8
-    // against 95.8 us, five rounds on one machine) and 2 us slower after a
-    // cache flush.
+    // against 95.8 us, five repetitions on one machine) and 2 us slower
+    // after a cache flush.
     const bool wave_tokens = lo_p == nullptr && nvec <= kWave * kBurst && g.T >= 2048 && D < kWaves;
     const int slice = wave_tokens ? nvec : slice_width(g.T, nvec, kWave, 1 << 30, 2048);
     const dim3 grid = wave_tokens ? item_grid((g.T + kWaves - 1) / kWaves, 1)
