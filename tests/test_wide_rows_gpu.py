@@ -5,8 +5,8 @@ vectors; wider rows take the kernels' loops over bursts (dispatch, the
 assign-and-copy launch, the relay fan-out, partials and finish, combine) and
 split the fp8 quantisation over several passes. These shapes reach those
 loops with at least 2048 tokens (one column slice per token), a ragged last
-burst (10 248 channels) and both modes; every result is compared with the
-oracle bit for bit.
+burst (10 248 channels), both modes and expert groups; every result is
+compared with the oracle bit for bit.
 """
 import numpy as np
 import pytest
@@ -14,6 +14,7 @@ import torch
 
 from combine_epx_get_amd import workloads as W
 from tests.test_parity_fused_gpu import run_fused
+from tests.test_parity_groups_gpu import run_group_case
 from tests.test_parity_gpu import run_case
 from tests.test_parity_relay_gpu import run_relay_case
 
@@ -51,3 +52,15 @@ def test_wide_row_parity(epx, shape, relay):
         run_fused(epx, x, idx, E, R, H, s, relay, dt, what=f"{shape}/fused {dt}")
     if relay:
         run_relay_case(epx, x, idx, w, E, R, H, s, f"{shape}/relay receive")
+
+
+def test_wide_row_groups(epx):
+    """Two expert groups at 16 512 channels: the group dispatch and the group
+    combine (with its float32 carry) over more than one burst."""
+    T, k, E, R, H, s, m, hidden = 2048, 4, 32, 4, 2, 1, 2, 16512
+    rng = np.random.Generator(np.random.PCG64(77))
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, hidden), dtype=np.float32))
+    idx = W.draw_routing(rng, T, E, k, "uniform")
+    w = W.draw_gate_weights(rng, T, k)
+    print("[wide rows] groups", flush=True)
+    run_group_case(epx, x, idx, w, E, R, H, s, m, "wide groups")
